@@ -1,0 +1,178 @@
+/*
+ * dpg.h -- C ABI of the deterministic BF16 projection GEMM library for AMD
+ * MI355X (gfx950).
+ *
+ * The operations are the dense projection GEMM family and the FP32 router GEMM
+ * described on the pages
+ *   "plan the 4096 -> 12288 input gradient with the row-half-release program
+ *    at T-exact keys" (description: BF16-operand forward, input gradient and
+ *    weight gradient; FP32 accumulation; BF16 or FP32 output),
+ *   "restore the K1 weight-gradient routes that meet the deterministic
+ *    package's absolute FP64 budgets" (description: the weight gradient reduces
+ *    over the token count T in 64-token K blocks, with one or two K splits), and
+ *   "cache the router entry points' calls by their own tensors" (description:
+ *    an FP32 router GEMM with 256 experts computed by BF16x3 emulation, and
+ *    deterministic=True as the default).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every matrix is row-major with a leading dimension `ld*` counted in
+ *   elements (ld >= number of columns).  All data pointers are DEVICE pointers
+ *   owned by the caller; the library keeps no pointer after a call returns.
+ * - `T` is the token count, `N` the output features, `K` the input features
+ *   (the pages write a projection as "K -> N", e.g. 4096 -> 12288).
+ * - Alignment: every base pointer is 16-byte aligned, every `ld * sizeof(elt)`
+ *   is a multiple of 16 bytes, and the contiguous extent of every matrix
+ *   (its number of columns) is a multiple of 8 elements.  Otherwise the call
+ *   returns DPG_ERR_ALIGNMENT.  T (the row count of X, dY, Y and dX) may be any
+ *   value >= 0, including odd counts of 64-token blocks.
+ * - Outputs are written only in [rows, cols]; elements of a padded row beyond
+ *   `cols` are never touched.  Outputs are overwritten, never read.
+ * - An empty output (a zero extent) is a no-op.  An empty reduction (K = 0 for
+ *   the forward pass, N = 0 for the input gradient, T = 0 for the weight
+ *   gradient) writes zeros.
+ * - `deterministic` != 0 (the default of the Python binding) selects the
+ *   deterministic plan: the K partition and the in-tile accumulation order are
+ *   a fixed function of (pass, T, N, K, output dtype, split_k) alone -- never of
+ *   the device, its CU count or the cache state -- so the bits are reproducible
+ *   on any MI355X.  deterministic == 0 selects the split-K plan, which may also
+ *   use the device's CU count to pick the K split.  `split_k` = 0 lets the
+ *   planner choose; 1..64 forces that many K splits in either mode.  In BOTH
+ *   modes every reduction runs in a fixed order with no atomics, so repeated
+ *   calls with the same arguments on one device give bitwise-identical
+ *   outputs; different plans may differ from each other in the last bits.
+ * - Split partials go to the caller's `workspace`, which must hold at least
+ *   dpg_workspace_size(...) bytes for the same shape and flags (it may be NULL
+ *   when that size is 0).  The library never allocates and never synchronizes;
+ *   all work is enqueued on `stream` (0 = the null stream), so calls may be
+ *   captured into a HIP graph.
+ * - All validation happens before the first launch: on any error nothing is
+ *   launched and nothing is written.  DPG_ERR_HIP reports a failed launch.
+ */
+#ifndef DPG_H_
+#define DPG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DPG_OK = 0,
+  DPG_ERR_INVALID_ARG = 1, /* negative size, ld < cols, NULL pointer for non-empty data, bad enum */
+  DPG_ERR_UNSUPPORTED = 2, /* split_k outside 0..64 */
+  DPG_ERR_ALIGNMENT = 3,   /* pointer / ld / contiguous extent not 16-byte compatible */
+  DPG_ERR_WORKSPACE = 4,   /* workspace smaller than dpg_workspace_size() */
+  DPG_ERR_HIP = 5          /* a kernel launch failed */
+} dpg_status;
+
+typedef enum { DPG_BF16 = 0, DPG_F32 = 1 } dpg_dtype;
+
+typedef enum {
+  DPG_PASS_FORWARD = 0,
+  DPG_PASS_DGRAD = 1,
+  DPG_PASS_WGRAD = 2,
+  DPG_PASS_ROUTER_FORWARD = 3,
+  DPG_PASS_ROUTER_DGRAD = 4,
+  DPG_PASS_ROUTER_WGRAD = 5
+} dpg_pass;
+
+/*
+ * Forward pass, Y[T,N] = X[T,K] . W[N,K]^T: both operands K-major (the
+ * row-half-release page, description, names this the K-major-B form).
+ *   x  : BF16 [T, K], row stride ldx     w : BF16 [N, K], row stride ldw
+ *   y  : y_dtype (BF16 or FP32) [T, N], row stride ldy
+ * FP32 accumulation; BF16 output is rounded to nearest even.
+ */
+dpg_status dpg_forward(const void* x, int64_t ldx, const void* w, int64_t ldw,
+                       void* y, int64_t ldy, dpg_dtype y_dtype,
+                       int64_t T, int64_t N, int64_t K, int deterministic, int split_k,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Input gradient, dX[T,K] = dY[T,N] . W[N,K]: the reduction runs over N, so W
+ * is read with its contiguous dimension along the output (the MN-major B form
+ * that the row-half-release page adds, description and commit message).
+ *   dy : BF16 [T, N], row stride lddy    w : BF16 [N, K], row stride ldw
+ *   dx : dx_dtype [T, K], row stride lddx
+ */
+dpg_status dpg_dgrad(const void* dy, int64_t lddy, const void* w, int64_t ldw,
+                     void* dx, int64_t lddx, dpg_dtype dx_dtype,
+                     int64_t T, int64_t N, int64_t K, int deterministic, int split_k,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Weight gradient, dW[N,K] = dY[T,N]^T . X[T,K], reducing over the token count
+ * T in 64-token blocks (the K1 weight-gradient page, description; an odd number
+ * of 64-token blocks is allowed).  With two K splits, split 0 takes blocks
+ * [0, ceil(B/2)) and split 1 the rest, B = ceil(T/64); partials are added in
+ * ascending split order.
+ *   dy : BF16 [T, N], row stride lddy    x : BF16 [T, K], row stride ldx
+ *   dw : dw_dtype [N, K], row stride lddw
+ */
+dpg_status dpg_wgrad(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                     void* dw, int64_t lddw, dpg_dtype dw_dtype,
+                     int64_t T, int64_t N, int64_t K, int deterministic, int split_k,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * FP32 router GEMM, E experts (256 on the router page), hidden size H, all
+ * operands and outputs FP32 (router page, description and the legend under its
+ * ratio table: token-by-hidden activations times a 256-by-hidden weight).  Every product a*b is
+ * computed by BF16x3 emulation: hi = bf16_rne(a), lo = bf16_rne(a - hi), and
+ * lo_a*hi_b + hi_a*lo_b + hi_a*hi_b accumulate (in that order) in FP32 on the
+ * BF16 matrix cores.
+ *   forward: y[T,E]  = x[T,H] . w[E,H]^T
+ *   dgrad  : dx[T,H] = dy[T,E] . w[E,H]
+ *   wgrad  : dw[E,H] = dy[T,E]^T . x[T,H]
+ */
+dpg_status dpg_router_forward(const float* x, int64_t ldx, const float* w, int64_t ldw,
+                              float* y, int64_t ldy, int64_t T, int64_t E, int64_t H,
+                              int deterministic, int split_k,
+                              void* workspace, size_t workspace_bytes, hipStream_t stream);
+dpg_status dpg_router_dgrad(const float* dy, int64_t lddy, const float* w, int64_t ldw,
+                            float* dx, int64_t lddx, int64_t T, int64_t E, int64_t H,
+                            int deterministic, int split_k,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+dpg_status dpg_router_wgrad(const float* dy, int64_t lddy, const float* x, int64_t ldx,
+                            float* dw, int64_t lddw, int64_t T, int64_t E, int64_t H,
+                            int deterministic, int split_k,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Bytes of workspace the call with these arguments needs (0 when the plan has a
+ * single K split).  For router passes N = E, K = H and out_dtype must be DPG_F32.
+ * Returns (size_t)-1 for arguments the matching call would reject.
+ */
+size_t dpg_workspace_size(dpg_pass pass, int64_t T, int64_t N, int64_t K, dpg_dtype out_dtype,
+                          int deterministic, int split_k);
+
+/*
+ * Host-only description of the plan the library would use (kernel variant,
+ * tile, raster group, K splits and their K-block partition, workspace) as one
+ * line of text in `buf` (truncated to buflen - 1 characters, NUL-terminated).
+ * Makes no HIP call; usable without a GPU.
+ */
+dpg_status dpg_plan_describe(dpg_pass pass, int64_t T, int64_t N, int64_t K, dpg_dtype out_dtype,
+                             int deterministic, int split_k, char* buf, size_t buflen);
+
+/* Drops every cached plan and bumps the cache generation.  Thread-safe. */
+void dpg_clear_plan_cache(void);
+
+/* Number of plans in the cache and the current cache generation (host-only). */
+void dpg_plan_cache_stats(int64_t* entries, int64_t* generation);
+
+/* Static text for a status code. */
+const char* dpg_status_string(dpg_status status);
+
+/* Library version string. */
+const char* dpg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DPG_H_ */
