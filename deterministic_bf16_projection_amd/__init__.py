@@ -1,0 +1,250 @@
+"""Python binding of libdpg, the MI355X projection GEMM library.
+
+Argument marshalling only: every entry point takes torch tensors (device
+memory allocated by PyTorch), passes their data pointers, row strides and the
+current HIP stream to the C ABI declared in ``include/dpg.h`` and returns the
+output tensor.  All arithmetic runs in the library's gfx950 kernels.  There is
+no fallback: if ``libdpg.so`` is missing, importing this package raises.
+
+Names follow the C ABI: ``dpg_forward``, ``dpg_dgrad``, ``dpg_wgrad``,
+``dpg_router_forward``, ``dpg_router_dgrad``, ``dpg_router_wgrad``.
+``deterministic=True`` is the default, as on the router page's description.
+"""
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdpg.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "dpg.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libdpg.so is not built; run `python -m deterministic_bf16_projection_amd.build` "
+                      "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+BF16, F32 = 0, 1
+PASS_FORWARD, PASS_DGRAD, PASS_WGRAD = 0, 1, 2
+PASS_ROUTER_FORWARD, PASS_ROUTER_DGRAD, PASS_ROUTER_WGRAD = 3, 4, 5
+_STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "alignment", 4: "workspace", 5: "HIP launch failed"}
+
+_i64, _vp, _ci, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+_GEMM_ARGS = [_vp, _i64, _vp, _i64, _vp, _i64, _ci, _i64, _i64, _i64, _ci, _ci, _vp, _sz, _vp]
+_ROUTER_ARGS = [_vp, _i64, _vp, _i64, _vp, _i64, _i64, _i64, _i64, _ci, _ci, _vp, _sz, _vp]
+for _name in ("dpg_forward", "dpg_dgrad", "dpg_wgrad"):
+    getattr(_lib, _name).argtypes = _GEMM_ARGS
+    getattr(_lib, _name).restype = _ci
+for _name in ("dpg_router_forward", "dpg_router_dgrad", "dpg_router_wgrad"):
+    getattr(_lib, _name).argtypes = _ROUTER_ARGS
+    getattr(_lib, _name).restype = _ci
+_lib.dpg_workspace_size.argtypes = [_ci, _i64, _i64, _i64, _ci, _ci, _ci]
+_lib.dpg_workspace_size.restype = _sz
+_lib.dpg_plan_describe.argtypes = [_ci, _i64, _i64, _i64, _ci, _ci, _ci, ctypes.c_char_p, _sz]
+_lib.dpg_plan_describe.restype = _ci
+_lib.dpg_clear_plan_cache.argtypes = []
+_lib.dpg_clear_plan_cache.restype = None
+_lib.dpg_plan_cache_stats.argtypes = [ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
+_lib.dpg_plan_cache_stats.restype = None
+_lib.dpg_status_string.argtypes = [_ci]
+_lib.dpg_status_string.restype = ctypes.c_char_p
+_lib.dpg_version.argtypes = []
+_lib.dpg_version.restype = ctypes.c_char_p
+
+
+class DpgError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _lib.dpg_status_string(status).decode()
+        super().__init__("%s: %s (status %d)" % (where, msg, status))
+
+
+def lib():
+    """The loaded ctypes library (for tests that call the C ABI directly)."""
+    return _lib
+
+
+def header_symbols():
+    """Names of the functions include/dpg.h declares."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"\b(dpg_[a-z_]+)\s*\(", text)))
+
+
+def version():
+    return _lib.dpg_version().decode()
+
+
+def _code(dtype):
+    if dtype == torch.bfloat16:
+        return BF16
+    if dtype == torch.float32:
+        return F32
+    raise TypeError("output dtype must be torch.bfloat16 or torch.float32")
+
+
+def _ld(t, name):
+    """Row stride in elements.  A matrix with at most one row never steps to a
+    next row, so its stride is reported as the column count rounded up to 8."""
+    if t.dim() != 2:
+        raise ValueError("%s must be 2-D" % name)
+    rows, cols = t.shape
+    if rows > 0 and cols > 1 and t.stride(1) != 1:
+        raise ValueError("%s must have unit column stride" % name)
+    if rows <= 1:
+        return max(8, (cols + 7) // 8 * 8)
+    return t.stride(0)
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def workspace_size(pass_, T, N, K, out_dtype=torch.bfloat16, deterministic=True, split_k=0):
+    n = _lib.dpg_workspace_size(pass_, T, N, K, _code(out_dtype), int(bool(deterministic)), split_k)
+    if n == ctypes.c_size_t(-1).value:
+        raise DpgError(1, "dpg_workspace_size")
+    return n
+
+
+def plan_describe(pass_, T, N, K, out_dtype=torch.bfloat16, deterministic=True, split_k=0):
+    buf = ctypes.create_string_buffer(1024)
+    st = _lib.dpg_plan_describe(pass_, T, N, K, _code(out_dtype), int(bool(deterministic)), split_k, buf, 1024)
+    if st:
+        raise DpgError(st, "dpg_plan_describe")
+    return buf.value.decode()
+
+
+def parse_plan(text):
+    """key=value pairs of a plan description as a dict of strings."""
+    return dict(kv.split("=", 1) for kv in text.split() if "=" in kv)
+
+
+def clear_plan_cache():
+    _lib.dpg_clear_plan_cache()
+
+
+def plan_cache_stats():
+    e, g = _i64(0), _i64(0)
+    _lib.dpg_plan_cache_stats(ctypes.byref(e), ctypes.byref(g))
+    return e.value, g.value
+
+
+def _workspace(pass_, T, N, K, out_code, det, split_k, workspace, device):
+    need = _lib.dpg_workspace_size(pass_, T, N, K, out_code, det, split_k)
+    if need == ctypes.c_size_t(-1).value:
+        raise DpgError(1, "dpg_workspace_size")
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise DpgError(4, "workspace")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def _call(name, pass_, a, b, out, out_code, T, N, K, deterministic, split_k, workspace, stream):
+    det = int(bool(deterministic))
+    ws, ws_bytes = _workspace(pass_, T, N, K, out_code, det, split_k, workspace, out.device)
+    fn = getattr(_lib, name)
+    args = [a.data_ptr(), _ld(a, "a"), b.data_ptr(), _ld(b, "b"), out.data_ptr(), _ld(out, "out")]
+    if pass_ < 3:
+        args.append(out_code)
+    args += [T, N, K, det, split_k, ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream)]
+    st = fn(*args)
+    if st:
+        raise DpgError(st, name)
+    return out
+
+
+def _check_in(t, dtype, name):
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s" % (name, dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+
+
+def dpg_forward(x, w, out=None, out_dtype=torch.bfloat16, deterministic=True, split_k=0, workspace=None,
+                stream=None):
+    """Y[T,N] = X[T,K] W[N,K]^T (BF16 operands, FP32 accumulation)."""
+    _check_in(x, torch.bfloat16, "x")
+    _check_in(w, torch.bfloat16, "w")
+    T, K = x.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("w must be [N, K]")
+    if out is None:
+        out = torch.empty((T, N), dtype=out_dtype, device=x.device)
+    return _call("dpg_forward", PASS_FORWARD, x, w, out, _code(out.dtype), T, N, K, deterministic, split_k,
+                 workspace, stream)
+
+
+def dpg_dgrad(dy, w, out=None, out_dtype=torch.bfloat16, deterministic=True, split_k=0, workspace=None,
+              stream=None):
+    """dX[T,K] = dY[T,N] W[N,K]."""
+    _check_in(dy, torch.bfloat16, "dy")
+    _check_in(w, torch.bfloat16, "w")
+    T, N = dy.shape
+    K = w.shape[1]
+    if w.shape[0] != N:
+        raise ValueError("w must be [N, K]")
+    if out is None:
+        out = torch.empty((T, K), dtype=out_dtype, device=dy.device)
+    return _call("dpg_dgrad", PASS_DGRAD, dy, w, out, _code(out.dtype), T, N, K, deterministic, split_k,
+                 workspace, stream)
+
+
+def dpg_wgrad(dy, x, out=None, out_dtype=torch.bfloat16, deterministic=True, split_k=0, workspace=None,
+              stream=None):
+    """dW[N,K] = dY[T,N]^T X[T,K], reducing over T."""
+    _check_in(dy, torch.bfloat16, "dy")
+    _check_in(x, torch.bfloat16, "x")
+    T, N = dy.shape
+    K = x.shape[1]
+    if x.shape[0] != T:
+        raise ValueError("x must be [T, K]")
+    if out is None:
+        out = torch.empty((N, K), dtype=out_dtype, device=dy.device)
+    return _call("dpg_wgrad", PASS_WGRAD, dy, x, out, _code(out.dtype), T, N, K, deterministic, split_k,
+                 workspace, stream)
+
+
+def dpg_router_forward(x, w, out=None, deterministic=True, split_k=0, workspace=None, stream=None):
+    """y[T,E] = x[T,H] w[E,H]^T, FP32 via BF16x3."""
+    _check_in(x, torch.float32, "x")
+    _check_in(w, torch.float32, "w")
+    T, H = x.shape
+    E = w.shape[0]
+    if out is None:
+        out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    return _call("dpg_router_forward", PASS_ROUTER_FORWARD, x, w, out, F32, T, E, H, deterministic, split_k,
+                 workspace, stream)
+
+
+def dpg_router_dgrad(dy, w, out=None, deterministic=True, split_k=0, workspace=None, stream=None):
+    """dx[T,H] = dy[T,E] w[E,H], FP32 via BF16x3."""
+    _check_in(dy, torch.float32, "dy")
+    _check_in(w, torch.float32, "w")
+    T, E = dy.shape
+    H = w.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=dy.device)
+    return _call("dpg_router_dgrad", PASS_ROUTER_DGRAD, dy, w, out, F32, T, E, H, deterministic, split_k,
+                 workspace, stream)
+
+
+def dpg_router_wgrad(dy, x, out=None, deterministic=True, split_k=0, workspace=None, stream=None):
+    """dw[E,H] = dy[T,E]^T x[T,H], FP32 via BF16x3."""
+    _check_in(dy, torch.float32, "dy")
+    _check_in(x, torch.float32, "x")
+    T, E = dy.shape
+    H = x.shape[1]
+    if out is None:
+        out = torch.empty((E, H), dtype=torch.float32, device=dy.device)
+    return _call("dpg_router_wgrad", PASS_ROUTER_WGRAD, dy, x, out, F32, T, E, H, deterministic, split_k,
+                 workspace, stream)

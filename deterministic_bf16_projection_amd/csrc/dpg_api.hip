@@ -1,0 +1,336 @@
+// C ABI of the projection GEMM library: argument validation, the plan cache,
+// and the launches.  Declarations and conventions are in include/dpg.h.
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <algorithm>
+#include <mutex>
+#include <unordered_map>
+
+#include "dpg.h"
+#include "gemm_kernel.h"
+#include "planner.h"
+
+namespace dpg {
+namespace {
+
+// ------------------------------------------------------- kernel registry --
+typedef TileCfg<256, 256, 64, 2, 2> TileL;
+typedef TileCfg<128, 128, 64, 2, 2> TileM;
+typedef TileCfg<64, 64, 64, 2, 2> TileS;
+
+typedef void (*KernelFn)(GemmParams);
+
+template <class Cfg, int LAYOUT, bool X3, int OUT>
+constexpr KernelFn kernel_for() {
+  return &gemm_kernel<Cfg, LAYOUT != LAYOUT_WGRAD, LAYOUT == LAYOUT_FWD, X3, OUT>;
+}
+
+template <class Cfg, int LAYOUT, bool X3>
+struct OutRow {
+  static constexpr KernelFn fns[3] = {X3 ? nullptr : kernel_for<Cfg, LAYOUT, X3, OUT_BF16>(),
+                                      kernel_for<Cfg, LAYOUT, X3, OUT_F32>(),
+                                      kernel_for<Cfg, LAYOUT, X3, OUT_PARTIAL>()};
+};
+
+// kernel pointer for (tile, layout, x3, out kind); null where not compiled
+KernelFn lookup_kernel(int tile, int layout, int x3, int out_kind) {
+#define DPG_ROW(CFG, L, X)                                              \
+  {OutRow<CFG, L, X>::fns[0], OutRow<CFG, L, X>::fns[1], OutRow<CFG, L, X>::fns[2]}
+  static const KernelFn table[kNumTiles][3][2][3] = {
+      {{DPG_ROW(TileL, 0, false), {nullptr, nullptr, nullptr}},
+       {DPG_ROW(TileL, 1, false), {nullptr, nullptr, nullptr}},
+       {DPG_ROW(TileL, 2, false), {nullptr, nullptr, nullptr}}},
+      {{DPG_ROW(TileM, 0, false), DPG_ROW(TileM, 0, true)},
+       {DPG_ROW(TileM, 1, false), DPG_ROW(TileM, 1, true)},
+       {DPG_ROW(TileM, 2, false), DPG_ROW(TileM, 2, true)}},
+      {{DPG_ROW(TileS, 0, false), DPG_ROW(TileS, 0, true)},
+       {DPG_ROW(TileS, 1, false), DPG_ROW(TileS, 1, true)},
+       {DPG_ROW(TileS, 2, false), DPG_ROW(TileS, 2, true)}},
+  };
+#undef DPG_ROW
+  return table[tile][layout][x3][out_kind];
+}
+
+int tile_threads(int tile) { return kTiles[tile].threads; }
+
+// ----------------------------------------------------------- plan cache --
+struct KeyHash {
+  size_t operator()(const PlanKey& k) const {
+    uint64_t h = 1469598103934665603ull;
+    auto mix = [&h](uint64_t v) { h = (h ^ v) * 1099511628211ull; };
+    mix((uint64_t)k.pass);
+    mix((uint64_t)k.T);
+    mix((uint64_t)k.N);
+    mix((uint64_t)k.K);
+    mix((uint64_t)k.out);
+    mix((uint64_t)k.det);
+    mix((uint64_t)k.split_req);
+    mix((uint64_t)k.cus);
+    return (size_t)h;
+  }
+};
+
+std::mutex g_mu;
+std::unordered_map<PlanKey, Plan, KeyHash>* g_cache = nullptr;
+int64_t g_generation = 0;
+
+// CU count of the current device (fast mode only), cached per device id.
+int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kDetCus;
+  if (cached[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = kDetCus;
+    cached[dev] = cus;
+  }
+  return cached[dev];
+}
+
+bool get_plan(const PlanKey& key, Plan* plan) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (!g_cache) g_cache = new std::unordered_map<PlanKey, Plan, KeyHash>();
+  auto it = g_cache->find(key);
+  if (it != g_cache->end()) {
+    *plan = it->second;
+    return true;
+  }
+  if (!make_plan(key, plan)) return false;
+  g_cache->emplace(key, *plan);
+  return true;
+}
+
+PlanKey make_key(int pass, int64_t T, int64_t N, int64_t K, int out, int det, int split_k, bool query_device) {
+  PlanKey k;
+  k.pass = pass;
+  k.T = T;
+  k.N = N;
+  k.K = K;
+  k.out = out;
+  k.det = det ? 1 : 0;
+  k.split_req = split_k;
+  k.cus = det ? kDetCus : (query_device ? device_cus() : kDetCus);
+  return k;
+}
+
+// ----------------------------------------------------------- validation --
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Mat {
+  const void* ptr;
+  int64_t ld, rows, cols;
+  int elt;  // bytes per element
+};
+
+dpg_status check_mat(const Mat& m) {
+  if (m.rows < 0 || m.cols < 0) return DPG_ERR_INVALID_ARG;
+  if (m.rows == 0 || m.cols == 0) return DPG_OK;  // empty: pointer and ld unused
+  if (!m.ptr) return DPG_ERR_INVALID_ARG;
+  if (m.ld < m.cols) return DPG_ERR_INVALID_ARG;
+  if (!aligned16(m.ptr) || (m.ld * m.elt) % 16 != 0 || m.cols % 8 != 0) return DPG_ERR_ALIGNMENT;
+  return DPG_OK;
+}
+
+// ---------------------------------------------------------------- launch --
+dpg_status run(int pass, const void* a, int64_t lda, const void* b, int64_t ldb, void* c, int64_t ldc, int out,
+               int64_t T, int64_t N, int64_t K, int det, int split_k, void* ws, size_t ws_bytes,
+               hipStream_t stream) {
+  if (out != DPG_BF16 && out != DPG_F32) return DPG_ERR_INVALID_ARG;
+  if (T < 0 || N < 0 || K < 0) return DPG_ERR_INVALID_ARG;
+  if (split_k < 0 || split_k > 64) return DPG_ERR_UNSUPPORTED;
+  const int in_elt = pass >= 3 ? 4 : 2;
+  const int out_elt = out == DPG_F32 ? 4 : 2;
+  // operand and output shapes as the caller sees them
+  Mat ma, mb, mc;
+  switch (pass % 3) {
+    case 0:  // Y[T,N] = X[T,K] W[N,K]^T
+      ma = {a, lda, T, K, in_elt};
+      mb = {b, ldb, N, K, in_elt};
+      mc = {c, ldc, T, N, out_elt};
+      break;
+    case 1:  // dX[T,K] = dY[T,N] W[N,K]
+      ma = {a, lda, T, N, in_elt};
+      mb = {b, ldb, N, K, in_elt};
+      mc = {c, ldc, T, K, out_elt};
+      break;
+    default:  // dW[N,K] = dY[T,N]^T X[T,K]
+      ma = {a, lda, T, N, in_elt};
+      mb = {b, ldb, T, K, in_elt};
+      mc = {c, ldc, N, K, out_elt};
+      break;
+  }
+  dpg_status st;
+  if ((st = check_mat(ma)) != DPG_OK) return st;
+  if ((st = check_mat(mb)) != DPG_OK) return st;
+  if ((st = check_mat(mc)) != DPG_OK) return st;
+  // a matrix whose other extent is nonzero needs its column count checked even when
+  // it is the reduction side of an empty product
+  if ((ma.cols % 8) || (mb.cols % 8) || (mc.cols % 8)) return DPG_ERR_ALIGNMENT;
+
+  Plan plan;
+  if (!get_plan(make_key(pass, T, N, K, out, det, split_k, true), &plan)) return DPG_ERR_INVALID_ARG;
+  if (plan.kind == PLAN_NOOP) return DPG_OK;
+  if (plan.ws_bytes > 0) {
+    if (ws_bytes < plan.ws_bytes) return DPG_ERR_WORKSPACE;
+    if (!ws || !aligned16(ws)) return DPG_ERR_WORKSPACE;
+  }
+
+  if (plan.kind == PLAN_ZERO) {
+    const int64_t quads = plan.M * (plan.N / 4);
+    const int grid = (int)std::min<int64_t>((quads + 255) / 256, 4096);
+    int M = (int)plan.M, Nn = (int)plan.N;
+    void* args[] = {&M, &Nn, &c, &ldc};
+    hipError_t e = hipLaunchKernel(out == DPG_BF16 ? (const void*)&zero_fill_kernel<OUT_BF16>
+                                                   : (const void*)&zero_fill_kernel<OUT_F32>,
+                                   dim3(grid), dim3(256), args, 0, stream);
+    return e == hipSuccess ? DPG_OK : DPG_ERR_HIP;
+  }
+
+  GemmParams p;
+  p.a = a;
+  p.b = b;
+  p.lda = lda;
+  p.ldb = ldb;
+  p.M = (int)plan.M;
+  p.N = (int)plan.N;
+  p.K = (int)plan.K;
+  p.tiles_m = plan.tiles_m;
+  p.tiles_n = plan.tiles_n;
+  p.splits = plan.splits;
+  p.kt_total = plan.kt_total;
+  p.kt_per_split = plan.kt_per_split;
+  p.group_m = plan.group_m;
+  int out_kind;
+  if (plan.splits > 1) {
+    p.c = ws;
+    p.ldc = plan.N;
+    p.split_stride = plan.M * plan.N;
+    out_kind = OUT_PARTIAL;
+  } else {
+    p.c = c;
+    p.ldc = ldc;
+    p.split_stride = 0;
+    out_kind = out == DPG_BF16 ? OUT_BF16 : OUT_F32;
+  }
+  KernelFn fn = lookup_kernel(plan.tile, plan.layout, plan.x3, out_kind);
+  if (!fn) return DPG_ERR_INVALID_ARG;
+  void* args[] = {&p};
+  hipError_t e = hipLaunchKernel((const void*)fn, dim3((unsigned)plan.grid), dim3(tile_threads(plan.tile)), args, 0,
+                                 stream);
+  if (e != hipSuccess) return DPG_ERR_HIP;
+  if (plan.splits > 1) {
+    const int64_t quads = plan.M * (plan.N / 4);
+    const int grid = (int)std::min<int64_t>((quads + 255) / 256, 8192);
+    const float* wsf = (const float*)ws;
+    int S = plan.splits, M = (int)plan.M, Nn = (int)plan.N;
+    int64_t stride = plan.M * plan.N;
+    void* rargs[] = {&wsf, &S, &stride, &M, &Nn, &c, &ldc};
+    e = hipLaunchKernel(out == DPG_BF16 ? (const void*)&splitk_reduce_kernel<OUT_BF16>
+                                        : (const void*)&splitk_reduce_kernel<OUT_F32>,
+                        dim3(grid), dim3(256), rargs, 0, stream);
+    if (e != hipSuccess) return DPG_ERR_HIP;
+  }
+  return DPG_OK;
+}
+
+}  // namespace
+}  // namespace dpg
+
+using namespace dpg;
+
+extern "C" {
+
+dpg_status dpg_forward(const void* x, int64_t ldx, const void* w, int64_t ldw, void* y, int64_t ldy,
+                       dpg_dtype y_dtype, int64_t T, int64_t N, int64_t K, int deterministic, int split_k,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run(DPG_PASS_FORWARD, x, ldx, w, ldw, y, ldy, y_dtype, T, N, K, deterministic, split_k, workspace,
+             workspace_bytes, stream);
+}
+
+dpg_status dpg_dgrad(const void* dy, int64_t lddy, const void* w, int64_t ldw, void* dx, int64_t lddx,
+                     dpg_dtype dx_dtype, int64_t T, int64_t N, int64_t K, int deterministic, int split_k,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run(DPG_PASS_DGRAD, dy, lddy, w, ldw, dx, lddx, dx_dtype, T, N, K, deterministic, split_k, workspace,
+             workspace_bytes, stream);
+}
+
+dpg_status dpg_wgrad(const void* dy, int64_t lddy, const void* x, int64_t ldx, void* dw, int64_t lddw,
+                     dpg_dtype dw_dtype, int64_t T, int64_t N, int64_t K, int deterministic, int split_k,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run(DPG_PASS_WGRAD, dy, lddy, x, ldx, dw, lddw, dw_dtype, T, N, K, deterministic, split_k, workspace,
+             workspace_bytes, stream);
+}
+
+dpg_status dpg_router_forward(const float* x, int64_t ldx, const float* w, int64_t ldw, float* y, int64_t ldy,
+                              int64_t T, int64_t E, int64_t H, int deterministic, int split_k, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  return run(DPG_PASS_ROUTER_FORWARD, x, ldx, w, ldw, y, ldy, DPG_F32, T, E, H, deterministic, split_k, workspace,
+             workspace_bytes, stream);
+}
+
+dpg_status dpg_router_dgrad(const float* dy, int64_t lddy, const float* w, int64_t ldw, float* dx, int64_t lddx,
+                            int64_t T, int64_t E, int64_t H, int deterministic, int split_k, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  return run(DPG_PASS_ROUTER_DGRAD, dy, lddy, w, ldw, dx, lddx, DPG_F32, T, E, H, deterministic, split_k, workspace,
+             workspace_bytes, stream);
+}
+
+dpg_status dpg_router_wgrad(const float* dy, int64_t lddy, const float* x, int64_t ldx, float* dw, int64_t lddw,
+                            int64_t T, int64_t E, int64_t H, int deterministic, int split_k, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  return run(DPG_PASS_ROUTER_WGRAD, dy, lddy, x, ldx, dw, lddw, DPG_F32, T, E, H, deterministic, split_k, workspace,
+             workspace_bytes, stream);
+}
+
+size_t dpg_workspace_size(dpg_pass pass, int64_t T, int64_t N, int64_t K, dpg_dtype out_dtype, int deterministic,
+                          int split_k) {
+  if ((int)pass >= 3 && out_dtype != DPG_F32) return (size_t)-1;
+  Plan plan;
+  if (!get_plan(make_key((int)pass, T, N, K, (int)out_dtype, deterministic, split_k, true), &plan))
+    return (size_t)-1;
+  return plan.kind == PLAN_GEMM ? plan.ws_bytes : 0;
+}
+
+dpg_status dpg_plan_describe(dpg_pass pass, int64_t T, int64_t N, int64_t K, dpg_dtype out_dtype, int deterministic,
+                             int split_k, char* buf, size_t buflen) {
+  if (!buf || buflen == 0) return DPG_ERR_INVALID_ARG;
+  if ((int)pass >= 3 && out_dtype != DPG_F32) return DPG_ERR_INVALID_ARG;
+  // host-only: the split-K mode is described for the nominal CU count
+  PlanKey key = make_key((int)pass, T, N, K, (int)out_dtype, deterministic, split_k, false);
+  Plan plan;
+  if (!make_plan(key, &plan)) return DPG_ERR_INVALID_ARG;
+  describe_plan(key, plan, buf, buflen);
+  return DPG_OK;
+}
+
+void dpg_clear_plan_cache(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_cache) g_cache->clear();
+  ++g_generation;
+}
+
+void dpg_plan_cache_stats(int64_t* entries, int64_t* generation) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (entries) *entries = g_cache ? (int64_t)g_cache->size() : 0;
+  if (generation) *generation = g_generation;
+}
+
+const char* dpg_status_string(dpg_status status) {
+  switch (status) {
+    case DPG_OK: return "ok";
+    case DPG_ERR_INVALID_ARG: return "invalid argument";
+    case DPG_ERR_UNSUPPORTED: return "unsupported split_k";
+    case DPG_ERR_ALIGNMENT: return "pointer, leading dimension or column count not 16-byte compatible";
+    case DPG_ERR_WORKSPACE: return "workspace missing or too small";
+    case DPG_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char* dpg_version(void) { return "dpg 0.1.0 gfx950"; }
+
+}  // extern "C"

@@ -1,0 +1,128 @@
+// Host planner: see planner.h.
+#include "planner.h"
+
+#include <stdio.h>
+
+#include <algorithm>
+#include <cmath>
+
+namespace dpg {
+
+const TileShape kTiles[kNumTiles] = {
+    {256, 256, 64, 256, 1, 1.00, false},
+    {128, 128, 64, 256, 1, 0.80, true},
+    {64, 64, 64, 256, 2, 0.45, true},
+};
+
+namespace {
+
+constexpr double kCuFlops = 2.2e15 / 256;  // sustained BF16 MFMA FLOP/s of one CU (measured loop)
+constexpr double kHbm = 5.0e12;            // sustained HBM bytes/s
+constexpr double kLaunchUs = 3.0;          // per extra kernel launch
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// GEMM view of a pass: C[M,N] = sum_k A(m,k) B(n,k).
+void gemm_view(int pass, int64_t T, int64_t N, int64_t K, int64_t* m, int64_t* n, int64_t* k, int* layout) {
+  switch (pass % 3) {
+    case 0:  // forward: Y[T,N] = X[T,K] W[N,K]^T
+      *m = T; *n = N; *k = K; *layout = LAYOUT_FWD;
+      break;
+    case 1:  // input gradient: dX[T,K] = dY[T,N] W[N,K]
+      *m = T; *n = K; *k = N; *layout = LAYOUT_DGRAD;
+      break;
+    default:  // weight gradient: dW[N,K] = dY[T,N]^T X[T,K]
+      *m = N; *n = K; *k = T; *layout = LAYOUT_WGRAD;
+      break;
+  }
+}
+
+double estimate_us(const TileShape& ts, int64_t M, int64_t N, int64_t K, int x3, int out_bytes, int in_bytes,
+                   int splits_req, int cus, int* splits_out, int* kt_per_out) {
+  const int64_t tiles = cdiv(M, ts.bm) * cdiv(N, ts.bn);
+  const int64_t kt_total = cdiv(K, ts.bk);
+  int64_t s = std::min<int64_t>(splits_req, kt_total);
+  const int64_t kt_per = cdiv(kt_total, s);
+  s = cdiv(kt_total, kt_per);  // no empty splits
+  const int64_t wgs = tiles * s;
+  const double flop_wg = 2.0 * ts.bm * ts.bn * (double)(kt_per * ts.bk) * (x3 ? 3 : 1);
+  const int64_t per_cu = cdiv(wgs, cus);
+  const double t_mfma = per_cu * flop_wg / (kCuFlops * ts.eff);
+  const double bytes = (double)(M * K + N * K) * in_bytes + (double)M * N * (s > 1 ? 4.0 * s : out_bytes);
+  const double t_mem = bytes / kHbm;
+  double t = std::max(t_mfma, t_mem) * 1e6 + kLaunchUs;
+  if (s > 1) t += ((double)M * N * (4.0 * s + out_bytes)) / kHbm * 1e6 + kLaunchUs;
+  *splits_out = (int)s;
+  *kt_per_out = (int)kt_per;
+  return t;
+}
+
+}  // namespace
+
+bool make_plan(const PlanKey& key, Plan* p) {
+  if (key.pass < 0 || key.pass > 5 || key.T < 0 || key.N < 0 || key.K < 0) return false;
+  if (key.out != 0 && key.out != 1) return false;
+  if (key.split_req < 0 || key.split_req > 64) return false;
+  *p = Plan();
+  p->x3 = key.pass >= 3;
+  p->out = key.out;
+  gemm_view(key.pass, key.T, key.N, key.K, &p->M, &p->N, &p->K, &p->layout);
+  if (p->M > INT32_MAX / 2 || p->N > INT32_MAX / 2 || p->K > INT32_MAX / 2) return false;
+  if (p->M == 0 || p->N == 0) {
+    p->kind = PLAN_NOOP;
+    return true;
+  }
+  if (p->K == 0) {
+    p->kind = PLAN_ZERO;
+    return true;
+  }
+  p->kind = PLAN_GEMM;
+  const int in_bytes = p->x3 ? 4 : 2;
+  const int out_bytes = key.out == 1 ? 4 : 2;
+  static const int kSplitChoices[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
+  double best = 1e300;
+  for (int ti = 0; ti < kNumTiles; ++ti) {
+    const TileShape& ts = kTiles[ti];
+    if (p->x3 && !ts.x3_ok) continue;
+    for (int sc : kSplitChoices) {
+      if (key.split_req != 0 && sc != key.split_req) continue;
+      int s, ktp;
+      const double t = estimate_us(ts, p->M, p->N, p->K, p->x3, out_bytes, in_bytes, sc, key.cus, &s, &ktp);
+      if (t < best * 0.999) {  // prefer the earlier (larger tile, fewer splits) choice on near ties
+        best = t;
+        p->tile = ti;
+        p->splits = s;
+        p->kt_per_split = ktp;
+      }
+    }
+    if (key.split_req != 0 && key.split_req > 64) return false;
+  }
+  const TileShape& ts = kTiles[p->tile];
+  p->tiles_m = (int)cdiv(p->M, ts.bm);
+  p->tiles_n = (int)cdiv(p->N, ts.bn);
+  p->kt_total = (int)cdiv(p->K, ts.bk);
+  p->group_m = std::min(p->tiles_m, 8);
+  p->grid = (int64_t)p->tiles_m * p->tiles_n * p->splits;
+  p->ws_bytes = p->splits > 1 ? (size_t)p->splits * (size_t)p->M * (size_t)p->N * 4u : 0;
+  p->est_us = best;
+  return p->grid <= INT32_MAX;
+}
+
+int describe_plan(const PlanKey& key, const Plan& p, char* buf, size_t buflen) {
+  static const char* kPass[] = {"forward", "dgrad", "wgrad", "router_forward", "router_dgrad", "router_wgrad"};
+  static const char* kLayout[] = {"Akmajor_Bkmajor", "Akmajor_Bmnmajor", "Amnmajor_Bmnmajor"};
+  if (p.kind == PLAN_NOOP)
+    return snprintf(buf, buflen, "pass=%s kind=noop", kPass[key.pass]);
+  if (p.kind == PLAN_ZERO)
+    return snprintf(buf, buflen, "pass=%s kind=zero_fill M=%lld N=%lld", kPass[key.pass], (long long)p.M,
+                    (long long)p.N);
+  const TileShape& ts = kTiles[p.tile];
+  return snprintf(buf, buflen,
+                  "pass=%s kind=gemm det=%d M=%lld N=%lld K=%lld layout=%s x3=%d out=%s tile=%dx%dx%d threads=%d "
+                  "tiles=%dx%d group_m=%d splits=%d kt_total=%d kt_per_split=%d grid=%lld workspace=%zu est_us=%.1f",
+                  kPass[key.pass], key.det, (long long)p.M, (long long)p.N, (long long)p.K, kLayout[p.layout], p.x3,
+                  p.out ? "f32" : "bf16", ts.bm, ts.bn, ts.bk, ts.threads, p.tiles_m, p.tiles_n, p.group_m, p.splits,
+                  p.kt_total, p.kt_per_split, (long long)p.grid, p.ws_bytes, p.est_us);
+}
+
+}  // namespace dpg

@@ -1,0 +1,61 @@
+// Host planner of the projection GEMM library: maps a call's key to a launch
+// plan (kernel variant, tile, raster group, K split and its partition,
+// workspace).  Pure C++, no HIP calls, so it can be exercised without a GPU.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace dpg {
+
+enum PlanKind { PLAN_NOOP = 0, PLAN_ZERO = 1, PLAN_GEMM = 2 };
+enum Layout { LAYOUT_FWD = 0, LAYOUT_DGRAD = 1, LAYOUT_WGRAD = 2 };
+
+// Tile shapes compiled into the library (all 256 threads, 32x32x16 MFMA).
+struct TileShape {
+  int bm, bn, bk;
+  int threads;
+  int occupancy;   // workgroups that fit one CU at once
+  double eff;      // sustained fraction of the CU's MFMA rate (model)
+  bool x3_ok;      // fits LDS with the BF16x3 hi and lo planes
+};
+constexpr int kNumTiles = 3;
+extern const TileShape kTiles[kNumTiles];
+
+struct PlanKey {
+  int pass;        // dpg_pass
+  int64_t T, N, K;
+  int out;         // dpg_dtype
+  int det;         // 0/1
+  int split_req;   // 0 = auto
+  int cus;         // CU count the plan was made for (fixed 256 in deterministic mode)
+  bool operator==(const PlanKey& o) const {
+    return pass == o.pass && T == o.T && N == o.N && K == o.K && out == o.out && det == o.det &&
+           split_req == o.split_req && cus == o.cus;
+  }
+};
+
+struct Plan {
+  int kind;
+  int layout;          // operand majorness (LAYOUT_*)
+  int x3;              // BF16x3 router arithmetic
+  int out;             // dpg_dtype of the output
+  int64_t M, N, K;     // GEMM view: C[M,N] = sum_k A(m,k) B(n,k)
+  int tile;            // index into kTiles
+  int tiles_m, tiles_n;
+  int splits, kt_total, kt_per_split;
+  int group_m;
+  int64_t grid;        // workgroups of the GEMM launch
+  size_t ws_bytes;     // FP32 partials: splits * M * N * 4 when splits > 1
+  double est_us;       // model estimate
+};
+
+// Deterministic CU count used by the deterministic planner (MI355X).
+constexpr int kDetCus = 256;
+
+// Builds the plan for a key; returns false for arguments no plan covers.
+bool make_plan(const PlanKey& key, Plan* plan);
+
+// One-line description of a plan.
+int describe_plan(const PlanKey& key, const Plan& plan, char* buf, size_t buflen);
+
+}  // namespace dpg

@@ -1,0 +1,315 @@
+"""Parity of the HIP path with the FP64 oracle, through the C ABI (GPU).
+
+Budgets are those of the K1 weight-gradient page (description): BF16 output
+atol = rtol = 1e-2 with no element outside; FP32 output relative Frobenius
+error <= 5e-5 and max error <= 1e-3 * max |ref|.  Exact-integer inputs make
+any FP32 accumulation order exact, so there the outputs must match the oracle
+bit for bit (FP32) or its nearest-even BF16 rounding (BF16).
+"""
+import numpy as np
+import pytest
+import torch
+
+import dpg_inputs
+import oracle
+from oracle import budgets
+from tests.gpu_util import dev_bf16, dev_f32, host_bits, host_f64, sample_positions
+
+pytestmark = pytest.mark.gpu
+
+dpg = pytest.importorskip("deterministic_bf16_projection_amd")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+OUT = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _run(pass_name, a, b, out_dtype, det=True, split=0, out=None):
+    fn = {"fwd": dpg.dpg_forward, "dgrad": dpg.dpg_dgrad, "wgrad": dpg.dpg_wgrad}[pass_name]
+    r = fn(a, b, out=out, out_dtype=out_dtype, deterministic=det, split_k=split)
+    torch.cuda.synchronize()
+    return r
+
+
+def _oracle(pass_name, a_bits, b_bits, rows=None, cols=None):
+    fn = {"fwd": oracle.forward, "dgrad": oracle.dgrad, "wgrad": oracle.wgrad}[pass_name]
+    return fn(a_bits, b_bits, rows=rows, cols=cols)
+
+
+def _operands(pass_name, x, w, dy):
+    return {"fwd": (x, w), "dgrad": (dy, w), "wgrad": (dy, x)}[pass_name]
+
+
+def _assert_exact(out_t, ref, out_name):
+    if out_name == "f32":
+        np.testing.assert_array_equal(host_f64(out_t), ref)
+    else:
+        np.testing.assert_array_equal(host_bits(out_t), oracle.f64_to_bf16(ref))
+
+
+# ---------------------------------------------------- exact-integer, bitwise --
+# Shapes span several tiles of every tile size with ragged row tails; the planner
+# picks 64-, 128- and 256-wide tiles across them.
+INT_SHAPES = [
+    (64, 1024, 4096),     # projection 4096->1024 at T = 64
+    (333, 200, 264),      # ragged everywhere (T odd, N and K multiples of 8 only)
+    (1, 8, 8),            # smallest
+    (1025, 64, 512),      # 17 blocks of 64 tokens, last holds 1
+    (700, 520, 136),
+    (2100, 1280, 256),    # large enough for 256x256 tiles
+]
+
+
+@pytest.mark.parametrize("T,N,K", INT_SHAPES)
+@pytest.mark.parametrize("pass_name", ["fwd", "dgrad", "wgrad"])
+@pytest.mark.parametrize("out_name", ["bf16", "f32"])
+def test_exact_integer_bitwise(T, N, K, pass_name, out_name):
+    x, w, dy = dpg_inputs.dense(T, N, K, seed_group=7, kind="int")
+    a, b = _operands(pass_name, x, w, dy)
+    ref = _oracle(pass_name, a, b)
+    da, db = dev_bf16(a), dev_bf16(b)
+    for det, split in [(True, 0), (False, 0), (False, 1), (False, 2), (True, 3)]:
+        out = _run(pass_name, da, db, OUT[out_name], det=det, split=split)
+        _assert_exact(out, ref, out_name)
+
+
+@pytest.mark.parametrize("T,N,K", [(4096, 4096, 1024), (16231, 12288, 4096)])
+@pytest.mark.parametrize("pass_name", ["fwd", "dgrad", "wgrad"])
+def test_exact_integer_sampled_large(T, N, K, pass_name):
+    """256x256 tiles at full size: exact-integer inputs, sampled positions."""
+    x, w, dy = dpg_inputs.dense(T, N, K, seed_group=8, kind="int")
+    a, b = _operands(pass_name, x, w, dy)
+    out = _run(pass_name, dev_bf16(a), dev_bf16(b), torch.float32)
+    rows, cols = out.shape
+    ii, jj = sample_positions(rows, cols, 3000, seed=1)
+    ref = _oracle(pass_name, a, b, rows=ii, cols=jj)
+    np.testing.assert_array_equal(host_f64(out)[ii, jj], ref)
+
+
+# ------------------------------------------- projection 4096 -> 1024, T = 64 --
+@pytest.mark.parametrize("seed", range(10))
+@pytest.mark.parametrize("pass_name", ["fwd", "dgrad", "wgrad"])
+def test_small_projection_budget(seed, pass_name):
+    x, w, dy = dpg_inputs.dense(64, 1024, 4096, seed_group=seed)
+    a, b = _operands(pass_name, x, w, dy)
+    ref = _oracle(pass_name, a, b)
+    da, db = dev_bf16(a), dev_bf16(b)
+    out = _run(pass_name, da, db, torch.bfloat16)
+    rep = budgets.check_bf16(host_f64(out), ref)
+    assert rep["ok"], rep
+    for _ in range(3):
+        again = _run(pass_name, da, db, torch.bfloat16)
+        assert torch.equal(again.view(torch.int16), out.view(torch.int16))
+
+
+# ----------------------------------------------------- FP32 router, BF16x3 --
+@pytest.mark.parametrize("T", [64, 256, 1024])
+@pytest.mark.parametrize("op", ["fwd", "dgrad", "wgrad"])
+@pytest.mark.parametrize("det,split", [(True, 0), (False, 0), (False, 2)])
+def test_router_budget(T, op, det, split):
+    E, H = 256, 4096
+    x, w, dy = dpg_inputs.router(T, E, H, seed_group=0)
+    fn = {"fwd": dpg.dpg_router_forward, "dgrad": dpg.dpg_router_dgrad, "wgrad": dpg.dpg_router_wgrad}[op]
+    orc = {"fwd": oracle.forward, "dgrad": oracle.dgrad, "wgrad": oracle.wgrad}[op]
+    a, b = {"fwd": (x, w), "dgrad": (dy, w), "wgrad": (dy, x)}[op]
+    out = fn(dev_f32(a), dev_f32(b), deterministic=det, split_k=split)
+    torch.cuda.synchronize()
+    got = host_f64(out)
+    ref = orc(a, b)
+    rep = budgets.check_f32(got, ref)
+    assert rep["ok"], rep
+    # against the exact BF16x3 value: only FP32 accumulation error remains
+    c3 = orc(a, b, mode="bf16x3")
+    s = orc(a, b, mode="abs")
+    R = {"fwd": H, "dgrad": E, "wgrad": T}[op]
+    gamma = 3 * R * 2.0 ** -24
+    assert np.all(np.abs(got - c3) <= gamma * 1.02 * s + 1e-30)
+
+
+@pytest.mark.parametrize("op", ["fwd", "dgrad", "wgrad"])
+@pytest.mark.parametrize("det,split", [(True, 0), (False, 3)])
+def test_router_exact_bf16x3(op, det, split):
+    """a = hi + lo inputs: the GPU equals the exact three-product value (lo*lo
+    dropped, hi*lo and lo*hi kept), bit for bit."""
+    T, E, H = 96, 256, 1024
+    x, w, dy = dpg_inputs.router(T, E, H, seed_group=3, kind="exact")
+    fn = {"fwd": dpg.dpg_router_forward, "dgrad": dpg.dpg_router_dgrad, "wgrad": dpg.dpg_router_wgrad}[op]
+    orc = {"fwd": oracle.forward, "dgrad": oracle.dgrad, "wgrad": oracle.wgrad}[op]
+    a, b = {"fwd": (x, w), "dgrad": (dy, w), "wgrad": (dy, x)}[op]
+    out = fn(dev_f32(a), dev_f32(b), deterministic=det, split_k=split)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host_f64(out), orc(a, b, mode="bf16x3"))
+
+
+# ----------------------------------------- projection 4096 -> 12288, full size --
+@pytest.fixture(scope="module")
+def big_inputs():
+    cache = {}
+
+    def get(T):
+        if T not in cache:
+            x, w, dy = dpg_inputs.dense(T, 12288, 4096, seed_group=0)
+            cache.clear()
+            cache[T] = (x, w, dy, dev_bf16(x), dev_bf16(w), dev_bf16(dy))
+        return cache[T]
+    return get
+
+
+@pytest.mark.parametrize("T", [16384, 16231])
+@pytest.mark.parametrize("pass_name,out_name", [("fwd", "bf16"), ("dgrad", "bf16"), ("dgrad", "f32"),
+                                                ("wgrad", "bf16")])
+def test_big_projection_sampled(big_inputs, T, pass_name, out_name):
+    x, w, dy, dx_, dw_, ddy = big_inputs(T)
+    a, b = _operands(pass_name, x, w, dy)
+    da, db = _operands(pass_name, dx_, dw_, ddy)
+    out = _run(pass_name, da, db, OUT[out_name])
+    rows, cols = out.shape
+    ii, jj = sample_positions(rows, cols, 4000, seed=T)
+    ref = _oracle(pass_name, a, b, rows=ii, cols=jj)
+    got = host_f64(out[torch.from_numpy(ii).cuda(), torch.from_numpy(jj).cuda()])
+    rep = budgets.check(got, ref, out_name)
+    assert rep["ok"], rep
+    assert torch.isfinite(out.float()).all()
+    again = _run(pass_name, da, db, OUT[out_name])
+    assert torch.equal(again.view(torch.int16) if out_name == "bf16" else again.view(torch.int32),
+                       out.view(torch.int16) if out_name == "bf16" else out.view(torch.int32))
+
+
+# ---------------------------------------------------- skinny-N weight gradient --
+SKINNY = [(4096, 64), (4096, 128), (5120, 48), (5120, 64)]
+SKINNY_T = [1025, 4031, 16173, 16384, 65537]
+
+
+@pytest.fixture(scope="module")
+def skinny_x():
+    cache = {}
+
+    def get(T, K):
+        if (T, K) not in cache:
+            cache.clear()
+            x = dpg_inputs.normal_bf16((T, K), 1.0, 0, 0)
+            cache[(T, K)] = (x, dev_bf16(x))
+        return cache[(T, K)]
+    return get
+
+
+@pytest.mark.parametrize("T", SKINNY_T)
+@pytest.mark.parametrize("K,N", SKINNY)
+def test_skinny_wgrad(skinny_x, T, K, N):
+    x, dx_ = skinny_x(T, K)
+    dy = dpg_inputs.normal_bf16((T, N), 1.0, 0, 2)
+    ddy = dev_bf16(dy)
+    ii, jj = sample_positions(N, K, 1500, seed=T + N)
+    ref = oracle.wgrad(dy, x, rows=ii, cols=jj)
+    sel = (torch.from_numpy(ii).cuda(), torch.from_numpy(jj).cuda())
+    for out_name in ("bf16", "f32"):
+        for det, split in [(True, 0), (False, 1), (False, 2)]:
+            out = _run("wgrad", ddy, dx_, OUT[out_name], det=det, split=split)
+            rep = budgets.check(host_f64(out[sel]), ref, out_name)
+            assert rep["ok"], (out_name, det, split, rep)
+            again = _run("wgrad", ddy, dx_, OUT[out_name], det=det, split=split)
+            assert torch.equal(again.view(torch.int16), out.view(torch.int16))
+
+
+# ------------------------------------------- checkpointed step 2fwd + bwd --
+@pytest.mark.parametrize("N", [1024, 512])
+def test_checkpointed_step(N):
+    T, K = 16384, 4096
+    x, w, dy = dpg_inputs.dense(T, N, K, seed_group=0)
+    dx_, dw_, ddy = dev_bf16(x), dev_bf16(w), dev_bf16(dy)
+
+    def step():
+        y1 = dpg.dpg_forward(dx_, dw_, out_dtype=torch.float32)
+        y2 = dpg.dpg_forward(dx_, dw_, out_dtype=torch.float32)
+        gx = dpg.dpg_dgrad(ddy, dw_, out_dtype=torch.float32)
+        gw = dpg.dpg_wgrad(ddy, dx_, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        return y1, y2, gx, gw
+
+    y1, y2, gx, gw = step()
+    assert torch.equal(y1.view(torch.int32), y2.view(torch.int32))
+    for name, out, a, b in [("fwd", y1, x, w), ("dgrad", gx, dy, w), ("wgrad", gw, dy, x)]:
+        rows, cols = out.shape
+        ii, jj = sample_positions(rows, cols, 2000, seed=N)
+        ref = _oracle(name, a, b, rows=ii, cols=jj)
+        rep = budgets.check_f32(host_f64(out)[ii, jj], ref)
+        assert rep["ok"], (name, rep)
+    z = step()
+    for u, v in zip((y1, y2, gx, gw), z):
+        assert torch.equal(u.view(torch.int32), v.view(torch.int32))
+
+
+# ---------------------------------------------------------- determinism --
+def test_twenty_reruns_bitwise():
+    T, N, K = 4031, 128, 4096
+    x, w, dy = dpg_inputs.dense(T, N, K, seed_group=1)
+    dx_, ddy = dev_bf16(x), dev_bf16(dy)
+    for det, split in [(True, 0), (False, 2)]:
+        first = _run("wgrad", ddy, dx_, torch.float32, det=det, split=split)
+        for _ in range(20):
+            again = _run("wgrad", ddy, dx_, torch.float32, det=det, split=split)
+            assert torch.equal(again.view(torch.int32), first.view(torch.int32))
+    xr, wr, dyr = dpg_inputs.router(256, 256, 4096, seed_group=1)
+    a, b = dev_f32(xr), dev_f32(wr)
+    first = dpg.dpg_router_forward(a, b, deterministic=False, split_k=4)
+    for _ in range(20):
+        again = dpg.dpg_router_forward(a, b, deterministic=False, split_k=4)
+        assert torch.equal(again.view(torch.int32), first.view(torch.int32))
+
+
+def test_other_stream_and_graph_replay():
+    T, N, K = 1025, 64, 4096
+    x, w, dy = dpg_inputs.dense(T, N, K, seed_group=2)
+    dx_, ddy = dev_bf16(x), dev_bf16(dy)
+    ref = _run("wgrad", ddy, dx_, torch.float32, det=False, split=2)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        out = dpg.dpg_wgrad(ddy, dx_, out_dtype=torch.float32, deterministic=False, split_k=2)
+    s.synchronize()
+    assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+    # HIP graph: capture the two launches (GEMM + fixed-order reduce) once
+    out = torch.empty_like(ref)
+    ws = torch.empty(dpg.workspace_size(dpg.PASS_WGRAD, T, N, K, torch.float32, False, 2),
+                     dtype=torch.uint8, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dpg.dpg_wgrad(ddy, dx_, out=out, deterministic=False, split_k=2, workspace=ws)
+    for i in range(4):
+        out.fill_(float("nan"))
+        ws.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), i
+        _run("fwd", dx_, dev_bf16(w), torch.bfloat16)  # eager work between replays
+
+
+# --------------------------------------------------------- output layout --
+@pytest.mark.parametrize("pass_name", ["fwd", "dgrad", "wgrad"])
+@pytest.mark.parametrize("out_name", ["bf16", "f32"])
+def test_padded_output_untouched(pass_name, out_name):
+    """Write into a column slice of a wider NaN-filled buffer: the slice holds
+    the result, everything outside it stays NaN."""
+    T, N, K = 197, 136, 264
+    x, w, dy = dpg_inputs.dense(T, N, K, seed_group=4, kind="int")
+    a, b = _operands(pass_name, x, w, dy)
+    ref = _oracle(pass_name, a, b)
+    rows, cols = ref.shape
+    big = torch.full((rows + 3, cols + 40), float("nan"), dtype=OUT[out_name], device="cuda")
+    view = big[1:rows + 1, 16:16 + cols]
+    _run(pass_name, dev_bf16(a), dev_bf16(b), OUT[out_name], out=view, det=False, split=2)
+    _assert_exact(view, ref, out_name)
+    mask = torch.ones_like(big, dtype=torch.bool)
+    mask[1:rows + 1, 16:16 + cols] = False
+    assert torch.isnan(big.float()[mask]).all()
+
+
+def test_empty_reductions_write_zeros():
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    dy = torch.empty((0, 32), dtype=torch.bfloat16, device="cuda")
+    dw = torch.full((32, 64), float("nan"), device="cuda")
+    dpg.dpg_wgrad(dy, x, out=dw)
+    torch.cuda.synchronize()
+    assert torch.equal(dw, torch.zeros_like(dw))
+    y = dpg.dpg_forward(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"),
+                        torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda"))
+    assert y.shape == (0, 16)

@@ -1,0 +1,142 @@
+"""Host-side checks of libdpg that need no GPU: exported symbols, the planner,
+workspace sizing, the plan cache and argument validation (every case here is
+rejected before any HIP call)."""
+import ctypes
+
+import pytest
+
+dpg = pytest.importorskip("deterministic_bf16_projection_amd")
+
+L = dpg.lib()
+BF16, F32 = dpg.BF16, dpg.F32
+
+
+def test_exports_every_header_symbol():
+    names = dpg.header_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version():
+    assert "gfx950" in dpg.version()
+
+
+def plan(pass_, T, N, K, out=BF16, det=1, split=0):
+    buf = ctypes.create_string_buffer(1024)
+    assert L.dpg_plan_describe(pass_, T, N, K, out, det, split, buf, 1024) == 0
+    return dpg.parse_plan(buf.value.decode())
+
+
+@pytest.mark.parametrize("pass_", [0, 1, 2])
+@pytest.mark.parametrize("T", [16384, 16231])
+def test_big_projection_whole_k_per_tile(pass_, T):
+    """4096 -> 12288 at T 16384 / 16231: the deterministic plan reduces the
+    whole K inside each output tile (one K split), as the row-half-release
+    page's plans do."""
+    p = plan(pass_, T, 12288, 4096)
+    assert p["kind"] == "gemm"
+    assert p["splits"] == "1"
+    assert p["workspace"] == "0"
+    assert p["tile"] == "256x256x64"
+
+
+@pytest.mark.parametrize("pass_", [0, 1, 2])
+def test_t_plus_minus_one_same_plan(pass_):
+    """Neighbouring token counts keep program, raster group and K partition
+    (planner test design on the row-half-release page)."""
+    base = plan(pass_, 16384, 12288, 4096)
+    for T in (16383, 16385):
+        p = plan(pass_, T, 12288, 4096)
+        for key in ("tile", "group_m", "splits", "layout"):
+            assert p[key] == base[key], (T, key)
+
+
+@pytest.mark.parametrize("T,blocks", [(1025, 17), (4031, 63), (16173, 253), (16384, 256), (65537, 1025)])
+def test_wgrad_two_way_partition(T, blocks):
+    """Two K splits over ceil(T/64) 64-token blocks: split 0 takes the first
+    ceil(B/2) blocks (odd block counts included)."""
+    p = plan(2, T, 64, 4096, out=F32, det=0, split=2)
+    assert int(p["kt_total"]) == blocks
+    assert int(p["splits"]) == 2
+    assert int(p["kt_per_split"]) == (blocks + 1) // 2
+    assert int(p["workspace"]) == 2 * 64 * 4096 * 4
+
+
+def test_forced_split_one():
+    p = plan(2, 16384, 128, 4096, out=BF16, det=0, split=1)
+    assert p["splits"] == "1" and p["workspace"] == "0"
+
+
+def test_router_uses_bf16x3():
+    p = plan(3, 64, 256, 4096, out=F32)
+    assert p["x3"] == "1"
+    assert plan(4, 1024, 256, 4096, out=F32)["layout"] == "Akmajor_Bmnmajor"
+    assert plan(5, 256, 256, 4096, out=F32)["layout"] == "Amnmajor_Bmnmajor"
+
+
+def test_deterministic_plan_ignores_device():
+    """The deterministic plan is a function of the shape only."""
+    a = plan(0, 64, 1024, 4096)
+    b = plan(0, 64, 1024, 4096)
+    assert a == b
+
+
+def test_empty_shapes():
+    assert plan(0, 0, 64, 64)["kind"] == "noop"
+    assert plan(2, 0, 64, 64)["kind"] == "zero_fill"   # empty reduction writes zeros
+    assert plan(0, 16, 64, 0)["kind"] == "zero_fill"
+    assert plan(1, 16, 0, 64)["kind"] == "zero_fill"
+    assert plan(2, 16, 0, 64)["kind"] == "noop"
+
+
+def test_workspace_size_matches_plan():
+    for args in [(2, 16384, 64, 4096, F32, 0, 2), (0, 64, 1024, 4096, BF16, 1, 0), (3, 64, 256, 4096, F32, 1, 0)]:
+        p = plan(args[0], args[1], args[2], args[3], out=args[4], det=args[5], split=args[6])
+        assert L.dpg_workspace_size(*args) == int(p["workspace"])
+    assert L.dpg_workspace_size(3, 64, 256, 4096, BF16, 1, 0) == ctypes.c_size_t(-1).value
+
+
+def test_plan_describe_rejects():
+    buf = ctypes.create_string_buffer(16)
+    assert L.dpg_plan_describe(0, -1, 8, 8, BF16, 1, 0, buf, 16) == 1
+    assert L.dpg_plan_describe(9, 1, 8, 8, BF16, 1, 0, buf, 16) == 1
+    assert L.dpg_plan_describe(0, 1, 8, 8, BF16, 1, 0, None, 0) == 1
+    # truncation keeps a NUL-terminated prefix
+    assert L.dpg_plan_describe(0, 64, 64, 64, BF16, 1, 0, buf, 16) == 0
+    assert len(buf.value) == 15
+
+
+def test_cache_generation():
+    e0, g0 = dpg.plan_cache_stats()
+    dpg.clear_plan_cache()
+    e1, g1 = dpg.plan_cache_stats()
+    assert e1 == 0 and g1 == g0 + 1
+
+
+# ------------------------------------------------------ validation (no launch) --
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every case fails validation first
+
+
+def fwd(x=FAKE, ldx=64, w=FAKE, ldw=64, y=FAKE, ldy=64, out=BF16, T=16, N=64, K=64, det=1, split=0, ws=None, wsb=0):
+    return L.dpg_forward(x, ldx, w, ldw, y, ldy, out, T, N, K, det, split, ws, wsb, None)
+
+
+def test_validation_errors():
+    assert fwd(T=-1) == 1
+    assert fwd(x=None) == 1                       # NULL for non-empty data
+    assert fwd(ldx=32) == 1                       # ld < cols
+    assert fwd(x=FAKE + 2) == 3                   # misaligned base
+    assert fwd(ldy=68) == 3                       # ld * 2 bytes not a multiple of 16
+    assert fwd(K=60, ldx=64, ldw=64) == 3         # contiguous extent not a multiple of 8
+    assert fwd(out=7) == 1                        # bad dtype
+    assert fwd(split=65) == 2
+    assert fwd(split=-1) == 2
+    # a forced split needs a workspace
+    assert L.dpg_wgrad(FAKE, 64, FAKE, 64, FAKE, 64, F32, 4096, 64, 64, 0, 2, None, 0, None) == 4
+    assert L.dpg_router_forward(FAKE, 64, FAKE + 4, 64, FAKE, 64, 16, 64, 64, 1, 0, None, 0, None) == 3
+
+
+def test_status_strings():
+    for s in range(6):
+        assert L.dpg_status_string(s)
