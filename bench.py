@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Benchmark of the projection GEMM hot path on one MI355X.
+
+A step is one pass of the whole dense projection path over one batch: the
+forward, input-gradient and weight-gradient GEMMs of the 4096 -> 12288
+projection at T = 16384 tokens (BF16 operands ~ N(0,1) / N(0,0.02), FP32
+accumulation, BF16 outputs, deterministic plans), inputs resident in HBM.
+``value`` is the step's TFLOP/s (3 x 2*T*N*K FLOP per step).
+
+Also reported: each pass's microseconds, TFLOP/s and fraction of the BF16 MFMA
+peak; the skinny-N weight gradients (4096->64, 4096->128, 5120->48, 5120->64
+at T = 16384, FP32 out) as GB/s of algorithmic HBM bytes against the 8 TB/s
+peak; the roofline of the dominant kernel from HIP events on the launch
+stream; and the FP64 oracle timed on the host cores on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz (dense)
+PEAK_HBM_GBPS = 8000.0
+T_BIG, N_BIG, K_BIG = 16384, 12288, 4096
+SKINNY = [(4096, 64), (4096, 128), (5120, 48), (5120, 64)]
+T_SKINNY = 16384
+KERNEL_SOURCES = ["deterministic_bf16_projection_amd/csrc/gemm_kernel.h",
+                  "deterministic_bf16_projection_amd/csrc/device_common.h"]
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel_pass):
+    """HBM bytes per launch of the dominant kernel from the committed rocprofv3
+    PMC summary, if it was taken from the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "gemm_%s_4096x12288_T16384_pmc.txt" % kernel_pass)
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_hash:\s*(\S+)", text)
+    b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m or not b or m.group(1) != kernel_source_hash():
+        return None
+    return float(b.group(1))
+
+
+def cpu_baseline(target_s=12.0):
+    """The FP64 oracle as it stands, on a bounded sample of the same workload:
+    the forward pass's first R rows of Y[16384, 12288] (all columns)."""
+    import numpy as np
+    import dpg_inputs
+    import oracle
+    # the first rows of the seeded X[16384, 4096] draw (numpy fills row-major)
+    x = dpg_inputs.normal_bf16((1024, K_BIG), 1.0, 0, 0)
+    w = dpg_inputs.normal_bf16((N_BIG, K_BIG), dpg_inputs.SIGMA_W, 0, 1)
+    oracle.forward(x[:1], w)
+    t0 = time.perf_counter()
+    oracle.forward(x[:8], w)
+    dt = time.perf_counter() - t0
+    rows = int(max(8, min(1024, target_s / max(dt / 8, 1e-6))))
+    t0 = time.perf_counter()
+    oracle.forward(x[:rows], w)
+    dt = time.perf_counter() - t0
+    flop = 2.0 * rows * N_BIG * K_BIG
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "forward 4096->12288: %d of 16384 rows of Y (%d x 12288 outputs, K=4096), FP64, %.1f s"
+                      % (rows, rows, dt)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--skip-skinny", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import dpg_inputs
+    import deterministic_bf16_projection_amd as dpg
+
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, w, dy = dpg_inputs.dense(T_BIG, N_BIG, K_BIG, seed_group=0)
+    X, W, DY = to_dev(x), to_dev(w), to_dev(dy)
+    del x, w, dy
+    Y = torch.empty((T_BIG, N_BIG), dtype=torch.bfloat16, device=dev)
+    DX = torch.empty((T_BIG, K_BIG), dtype=torch.bfloat16, device=dev)
+    DW = torch.empty((N_BIG, K_BIG), dtype=torch.bfloat16, device=dev)
+    passes = [
+        ("fwd", lambda: dpg.dpg_forward(X, W, out=Y)),
+        ("dgrad", lambda: dpg.dpg_dgrad(DY, W, out=DX)),
+        ("wgrad", lambda: dpg.dpg_wgrad(DY, X, out=DW)),
+    ]
+    plans = {name: dpg.plan_describe(i, T_BIG, N_BIG, K_BIG) for i, (name, _) in enumerate(passes)}
+    flop_pass = 2.0 * T_BIG * N_BIG * K_BIG
+
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        for _, fn in passes:
+            fn()
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps; events around every pass on the launch stream
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in passes]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for p, (_, fn) in enumerate(passes):
+            ev[s][p][0].record(stream)
+            fn()
+            ev[s][p][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    per_pass = {}
+    for p, (name, _) in enumerate(passes):
+        ts = [ev[s][p][0].elapsed_time(ev[s][p][1]) for s in range(args.steps)]
+        us = 1e3 * float(np.mean(ts))
+        per_pass[name] = {"us_mean": round(us, 1), "us_min": round(1e3 * min(ts), 1),
+                          "tflops": round(flop_pass / us / 1e6, 1),
+                          "frac_peak": round(flop_pass / us / 1e6 / PEAK_BF16_TFLOPS, 4),
+                          "plan": plans[name]}
+    value = 3 * flop_pass / (ms_step * 1e-3) / 1e12
+
+    dominant = max(per_pass, key=lambda k: per_pass[k]["us_mean"])
+    achieved = flop_pass / (per_pass[dominant]["us_mean"] * 1e-6) / 1e12
+    traffic = read_traffic(dominant)
+    roofline = {"bound": "mfma", "kernel": "gemm_kernel (%s, 256x256x64 tile)" % dominant,
+                "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "algorithmic_flop_per_launch": flop_pass}
+
+    skinny = []
+    if not args.skip_skinny:
+        del Y, DX, DW
+        torch.cuda.empty_cache()
+        for K, N in SKINNY:
+            xs = to_dev(dpg_inputs.normal_bf16((T_SKINNY, K), 1.0, 0, 0))
+            dys = to_dev(dpg_inputs.normal_bf16((T_SKINNY, N), 1.0, 0, 2))
+            out = torch.empty((N, K), dtype=torch.float32, device=dev)
+            for det, split in [(True, 0), (False, 2)]:
+                ws_n = dpg.workspace_size(dpg.PASS_WGRAD, T_SKINNY, N, K, torch.float32, det, split)
+                ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
+                for _ in range(5):
+                    dpg.dpg_wgrad(dys, xs, out=out, deterministic=det, split_k=split, workspace=ws)
+                reps = 50
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    dpg.dpg_wgrad(dys, xs, out=out, deterministic=det, split_k=split, workspace=ws)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                nbytes = 2.0 * T_SKINNY * K + 2.0 * T_SKINNY * N + 4.0 * N * K
+                skinny.append({"shape": "%d->%d" % (K, N), "T": T_SKINNY, "out": "f32",
+                               "mode": "deterministic" if det else "split_k=2", "us": round(us, 2),
+                               "GBps": round(nbytes / us / 1e3, 1),
+                               "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 4),
+                               "plan": dpg.plan_describe(dpg.PASS_WGRAD, T_SKINNY, N, K, torch.float32, det, split)})
+            del xs, dys, out
+
+    cpu = None if args.no_cpu_baseline else cpu_baseline()
+
+    line = {
+        "metric": "TFLOP/s and % BF16 MFMA peak per pass, 4096->12288 T=16384; skinny wgrad GB/s",
+        "value": round(value, 1),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "projection 4096->12288 (K=4096, N=12288), T=16384 tokens: forward + input "
+                               "gradient + weight gradient, BF16 in/out, FP32 accumulation, deterministic plan",
+                   "T": T_BIG, "N": N_BIG, "K": K_BIG, "global_batch": T_BIG, "parallelism": "single GPU"},
+        "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "passes": per_pass,
+        "skinny_wgrad": skinny,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
