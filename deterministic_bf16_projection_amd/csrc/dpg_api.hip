@@ -10,6 +10,7 @@
 #include <unordered_map>
 
 #include "dpg.h"
+#include "gemm_fast.h"
 #include "gemm_kernel.h"
 #include "planner.h"
 
@@ -52,6 +53,27 @@ KernelFn lookup_kernel(int tile, int layout, int x3, int out_kind) {
   };
 #undef DPG_ROW
   return table[tile][layout][x3][out_kind];
+}
+
+// software-pipelined kernels for the 256x256 and 128x128 tiles
+template <int BM, int BN, int WM_, int WN_, int LAYOUT>
+struct FastRow {
+  static constexpr KernelFn fns[3] = {
+      &gemm_fast_kernel<BM, BN, WM_, WN_, LAYOUT != LAYOUT_WGRAD, LAYOUT == LAYOUT_FWD, OUT_BF16>,
+      &gemm_fast_kernel<BM, BN, WM_, WN_, LAYOUT != LAYOUT_WGRAD, LAYOUT == LAYOUT_FWD, OUT_F32>,
+      &gemm_fast_kernel<BM, BN, WM_, WN_, LAYOUT != LAYOUT_WGRAD, LAYOUT == LAYOUT_FWD, OUT_PARTIAL>};
+};
+
+KernelFn lookup_fast_kernel(int tile, int layout, int out_kind) {
+#define DPG_FROW(BM, BN, WM_, WN_, L) \
+  {FastRow<BM, BN, WM_, WN_, L>::fns[0], FastRow<BM, BN, WM_, WN_, L>::fns[1], FastRow<BM, BN, WM_, WN_, L>::fns[2]}
+  static const KernelFn table[2][3][3] = {
+      {DPG_FROW(256, 256, 2, 4, 0), DPG_FROW(256, 256, 2, 4, 1), DPG_FROW(256, 256, 2, 4, 2)},
+      {DPG_FROW(128, 128, 2, 2, 0), DPG_FROW(128, 128, 2, 2, 1), DPG_FROW(128, 128, 2, 2, 2)},
+  };
+#undef DPG_FROW
+  if (tile < 0 || tile > 1) return nullptr;
+  return table[tile][layout][out_kind];
 }
 
 int tile_threads(int tile) { return kTiles[tile].threads; }
@@ -216,11 +238,14 @@ dpg_status run(int pass, const void* a, int64_t lda, const void* b, int64_t ldb,
     p.split_stride = 0;
     out_kind = out == DPG_BF16 ? OUT_BF16 : OUT_F32;
   }
-  KernelFn fn = lookup_kernel(plan.tile, plan.layout, plan.x3, out_kind);
+  // the pipelined kernel addresses each tile through 32-bit buffer offsets
+  const bool ld_ok = lda < (1 << 23) && ldb < (1 << 23);
+  KernelFn fn = (plan.fast && ld_ok) ? lookup_fast_kernel(plan.tile, plan.layout, out_kind)
+                                     : lookup_kernel(plan.tile, plan.layout, plan.x3, out_kind);
   if (!fn) return DPG_ERR_INVALID_ARG;
   void* args[] = {&p};
-  hipError_t e = hipLaunchKernel((const void*)fn, dim3((unsigned)plan.grid), dim3(tile_threads(plan.tile)), args, 0,
-                                 stream);
+  const int threads = (plan.fast && ld_ok && plan.tile == 0) ? 512 : tile_threads(plan.tile);
+  hipError_t e = hipLaunchKernel((const void*)fn, dim3((unsigned)plan.grid), dim3(threads), args, 0, stream);
   if (e != hipSuccess) return DPG_ERR_HIP;
   if (plan.splits > 1) {
     const int64_t quads = plan.M * (plan.N / 4);

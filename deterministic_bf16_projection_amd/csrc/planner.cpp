@@ -9,9 +9,9 @@
 namespace dpg {
 
 const TileShape kTiles[kNumTiles] = {
-    {256, 256, 64, 256, 1, 1.00, false},
-    {128, 128, 64, 256, 1, 0.80, true},
-    {64, 64, 64, 256, 2, 0.45, true},
+    {256, 256, 64, 256, 1, 1.00, false, true},
+    {128, 128, 64, 256, 1, 0.80, true, true},
+    {64, 64, 64, 256, 2, 0.45, true, false},
 };
 
 namespace {
@@ -102,6 +102,9 @@ bool make_plan(const PlanKey& key, Plan* p) {
   p->tiles_n = (int)cdiv(p->N, ts.bn);
   p->kt_total = (int)cdiv(p->K, ts.bk);
   p->group_m = std::min(p->tiles_m, 8);
+  // the pipelined kernel needs whole 64-wide K tiles on K-major operands
+  const bool kmajor_ok = p->layout == LAYOUT_WGRAD || (p->K % 64) == 0;
+  p->fast = (!p->x3 && ts.fast_ok && kmajor_ok) ? 1 : 0;
   p->grid = (int64_t)p->tiles_m * p->tiles_n * p->splits;
   p->ws_bytes = p->splits > 1 ? (size_t)p->splits * (size_t)p->M * (size_t)p->N * 4u : 0;
   p->est_us = best;
@@ -119,9 +122,9 @@ int describe_plan(const PlanKey& key, const Plan& p, char* buf, size_t buflen) {
   const TileShape& ts = kTiles[p.tile];
   return snprintf(buf, buflen,
                   "pass=%s kind=gemm det=%d M=%lld N=%lld K=%lld layout=%s x3=%d out=%s tile=%dx%dx%d threads=%d "
-                  "tiles=%dx%d group_m=%d splits=%d kt_total=%d kt_per_split=%d grid=%lld workspace=%zu est_us=%.1f",
+                  "kernel=%s tiles=%dx%d group_m=%d splits=%d kt_total=%d kt_per_split=%d grid=%lld workspace=%zu est_us=%.1f",
                   kPass[key.pass], key.det, (long long)p.M, (long long)p.N, (long long)p.K, kLayout[p.layout], p.x3,
-                  p.out ? "f32" : "bf16", ts.bm, ts.bn, ts.bk, ts.threads, p.tiles_m, p.tiles_n, p.group_m, p.splits,
+                  p.out ? "f32" : "bf16", ts.bm, ts.bn, ts.bk, ts.threads, p.fast ? "pipelined" : "generic", p.tiles_m, p.tiles_n, p.group_m, p.splits,
                   p.kt_total, p.kt_per_split, (long long)p.grid, p.ws_bytes, p.est_us);
 }
 

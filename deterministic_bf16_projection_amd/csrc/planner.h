@@ -17,6 +17,7 @@ struct TileShape {
   int occupancy;   // workgroups that fit one CU at once
   double eff;      // sustained fraction of the CU's MFMA rate (model)
   bool x3_ok;      // fits LDS with the BF16x3 hi and lo planes
+  bool fast_ok;    // a software-pipelined variant exists for this tile
 };
 constexpr int kNumTiles = 3;
 extern const TileShape kTiles[kNumTiles];
@@ -41,6 +42,7 @@ struct Plan {
   int out;             // dpg_dtype of the output
   int64_t M, N, K;     // GEMM view: C[M,N] = sum_k A(m,k) B(n,k)
   int tile;            // index into kTiles
+  int fast;            // software-pipelined kernel (gemm_fast.h) instead of the generic one
   int tiles_m, tiles_n;
   int splits, kt_total, kt_per_split;
   int group_m;
