@@ -12,6 +12,7 @@
 #include "dpg.h"
 #include "gemm_fast.h"
 #include "gemm_kernel.h"
+#include "skinny_wgrad.h"
 #include "planner.h"
 
 namespace dpg {
@@ -157,6 +158,20 @@ dpg_status check_mat(const Mat& m) {
   return DPG_OK;
 }
 
+// fixed-order sum of the split partials in the workspace, converted to the output type
+dpg_status launch_reduce(const Plan& plan, void* ws, void* c, int64_t ldc, int out, hipStream_t stream) {
+  const int64_t quads = plan.M * (plan.N / 4);
+  const int grid = (int)std::min<int64_t>((quads + 255) / 256, 8192);
+  const float* wsf = (const float*)ws;
+  int S = plan.splits, M = (int)plan.M, Nn = (int)plan.N;
+  int64_t stride = plan.M * plan.N;
+  void* rargs[] = {&wsf, &S, &stride, &M, &Nn, &c, &ldc};
+  hipError_t e = hipLaunchKernel(out == DPG_BF16 ? (const void*)&splitk_reduce_kernel<OUT_BF16>
+                                                 : (const void*)&splitk_reduce_kernel<OUT_F32>,
+                                 dim3(grid), dim3(256), rargs, 0, stream);
+  return e == hipSuccess ? DPG_OK : DPG_ERR_HIP;
+}
+
 // ---------------------------------------------------------------- launch --
 dpg_status run(int pass, const void* a, int64_t lda, const void* b, int64_t ldb, void* c, int64_t ldc, int out,
                int64_t T, int64_t N, int64_t K, int det, int split_k, void* ws, size_t ws_bytes,
@@ -212,6 +227,39 @@ dpg_status run(int pass, const void* a, int64_t lda, const void* b, int64_t ldb,
     return e == hipSuccess ? DPG_OK : DPG_ERR_HIP;
   }
 
+  if (plan.skinny && lda < (1 << 23) && ldb < (1 << 23)) {
+    SkinnyParams q;
+    q.dy = a;
+    q.x = b;
+    q.lddy = lda;
+    q.ldx = ldb;
+    q.T = (int)plan.K;
+    q.N = (int)plan.M;
+    q.K = (int)plan.N;
+    q.n_blocks = plan.tiles_m;
+    q.k_blocks = plan.tiles_n;
+    q.splits = plan.splits;
+    q.tb_total = plan.kt_total;
+    q.tb_per_split = plan.kt_per_split;
+    const void* kfn;
+    if (plan.splits > 1) {
+      q.out = ws;
+      q.ldo = plan.N;
+      q.split_stride = plan.M * plan.N;
+      kfn = (const void*)&skinny_wgrad_kernel<OUT_PARTIAL>;
+    } else {
+      q.out = c;
+      q.ldo = ldc;
+      q.split_stride = 0;
+      kfn = out == DPG_BF16 ? (const void*)&skinny_wgrad_kernel<OUT_BF16> : (const void*)&skinny_wgrad_kernel<OUT_F32>;
+    }
+    void* sargs[] = {&q};
+    hipError_t e = hipLaunchKernel(kfn, dim3((unsigned)plan.grid), dim3(512), sargs, 0, stream);
+    if (e != hipSuccess) return DPG_ERR_HIP;
+    if (plan.splits > 1) return launch_reduce(plan, ws, c, ldc, out, stream);
+    return DPG_OK;
+  }
+
   GemmParams p;
   p.a = a;
   p.b = b;
@@ -244,21 +292,14 @@ dpg_status run(int pass, const void* a, int64_t lda, const void* b, int64_t ldb,
                                      : lookup_kernel(plan.tile, plan.layout, plan.x3, out_kind);
   if (!fn) return DPG_ERR_INVALID_ARG;
   void* args[] = {&p};
-  const int threads = (plan.fast && ld_ok && plan.tile == 0) ? 512 : tile_threads(plan.tile);
-  hipError_t e = hipLaunchKernel((const void*)fn, dim3((unsigned)plan.grid), dim3(threads), args, 0, stream);
+  const bool fast = plan.fast && ld_ok;
+  const int threads = (fast && plan.tile == 0) ? 512 : tile_threads(plan.tile);
+  // the pipelined kernel is persistent: one workgroup per CU slot walks its units
+  int64_t grid = plan.grid;
+  if (fast) grid = std::min<int64_t>(grid, (int64_t)device_cus() * (plan.tile == 0 ? 1 : 2));
+  hipError_t e = hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3(threads), args, 0, stream);
   if (e != hipSuccess) return DPG_ERR_HIP;
-  if (plan.splits > 1) {
-    const int64_t quads = plan.M * (plan.N / 4);
-    const int grid = (int)std::min<int64_t>((quads + 255) / 256, 8192);
-    const float* wsf = (const float*)ws;
-    int S = plan.splits, M = (int)plan.M, Nn = (int)plan.N;
-    int64_t stride = plan.M * plan.N;
-    void* rargs[] = {&wsf, &S, &stride, &M, &Nn, &c, &ldc};
-    e = hipLaunchKernel(out == DPG_BF16 ? (const void*)&splitk_reduce_kernel<OUT_BF16>
-                                        : (const void*)&splitk_reduce_kernel<OUT_F32>,
-                        dim3(grid), dim3(256), rargs, 0, stream);
-    if (e != hipSuccess) return DPG_ERR_HIP;
-  }
+  if (plan.splits > 1) return launch_reduce(plan, ws, c, ldc, out, stream);
   return DPG_OK;
 }
 

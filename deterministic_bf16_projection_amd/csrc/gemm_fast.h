@@ -168,12 +168,64 @@ __device__ __forceinline__ void sched_step() {
   }
 }
 
+// Work units of a launch: one (output tile, K split) pair each.  The grid is
+// persistent: workgroup b takes units b, b + grid, b + 2 grid, ...  Unit ids
+// are mapped through the XCD remap and a grouped raster so that the units the
+// workgroups of one XCD run at the same time form a compact block of tiles
+// (shared A rows and B columns stay in that XCD's L2).
+struct UnitMap {
+  int tiles_m, tiles_n, group_m, splits, kt_per, kt_total, total;
+};
+
+// Position of a stream of (unit, K tile) steps.
+struct StepCursor {
+  int u;            // unit id (>= total when past the end)
+  int kt;           // K tile index within the unit's split
+  int nkt, kt0;     // the unit's K tiles and first K tile
+  int row0, col0;   // the unit's tile origin
+  int split;
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ StepCursor cursor_at(const UnitMap& m, int unit) {
+  StepCursor c;
+  c.u = unit;
+  c.kt = 0;
+  const int tiles = m.tiles_m * m.tiles_n;
+  const int pid = xcd_remap(min(unit, m.total - 1), m.total);
+  const int split = pid / tiles;
+  const int t = pid - split * tiles;
+  const int per_group = m.group_m * m.tiles_n;
+  const int group = t / per_group;
+  const int first_m = group * m.group_m;
+  const int gsize = min(m.tiles_m - first_m, m.group_m);
+  const int r = t - group * per_group;
+  c.row0 = (first_m + r % gsize) * BM;
+  c.col0 = (r / gsize) * BN;
+  c.split = split;
+  c.kt0 = split * m.kt_per;
+  c.nkt = min(c.kt0 + m.kt_per, m.kt_total) - c.kt0;
+  return c;
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ StepCursor cursor_next(const UnitMap& m, const StepCursor& c, int stride) {
+  if (c.kt + 1 < c.nkt) {
+    StepCursor n = c;
+    n.kt = c.kt + 1;
+    return n;
+  }
+  return cursor_at<BM, BN>(m, c.u + stride);
+}
+
+__device__ __forceinline__ bool cursor_valid(const UnitMap& m, const StepCursor& c) { return c.u < m.total; }
+
 // Which operands a wave stages: both (four-wave tiles), or only A / only B
 // (eight-wave tiles: waves 0-3 stage A, waves 4-7 stage B).
 enum StageRole { ROLE_BOTH = 0, ROLE_A = 1, ROLE_B = 2 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KMAJ, bool B_KMAJ, int ROLE>
-struct FastMainLoop {
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KMAJ, bool B_KMAJ, int OUT, int ROLE>
+struct FastGemm {
   static constexpr int BK = 64;
   static constexpr int NT = 64 * WAVES_M * WAVES_N;
   static constexpr int NTL = ROLE == ROLE_BOTH ? NT : NT / 2;  // threads staging one operand
@@ -184,15 +236,60 @@ struct FastMainLoop {
   typedef FastOperand<BN, B_KMAJ, NTL> OpB;
   static constexpr bool DO_A = ROLE != ROLE_B, DO_B = ROLE != ROLE_A;
 
-  static __device__ __forceinline__ void run(__bf16* smem, const GemmParams& p, int ltid, int lane, int wm, int wn,
-                                             int row0, int col0, int kt0, int nkt, f32x16 (&acc)[FM][FN]) {
+  // Accumulators hold the transposed product: acc[i][j] is the 32x32 block
+  // D[n][m] = sum_k B(n,k) A(m,k), so that lane l owns output row m = l % 32
+  // and the four consecutive columns n = (r/4)*8 + (l/32)*4 + [0,4).
+  static __device__ __forceinline__ void epilogue(const GemmParams& p, const StepCursor& c, int lane, int wm, int wn,
+                                                  f32x16 (&acc)[FM][FN]) {
+    char* out;
+    int64_t ldc;
+    if (OUT == OUT_PARTIAL) {
+      out = (char*)p.c + (int64_t)c.split * p.split_stride * 4;
+      ldc = p.ldc;
+    } else {
+      out = (char*)p.c;
+      ldc = p.ldc;
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int m = c.row0 + wm * WM + i * 32 + (lane & 31);
+      if (m >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int n = c.col0 + wn * WN + j * 32 + q * 8 + (lane >> 5) * 4;
+          if (n >= p.N) continue;
+          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
+          if (OUT == OUT_BF16) {
+            *(u32x2*)(out + ((int64_t)m * ldc + n) * 2) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          } else {
+            *(f32x4*)(out + ((int64_t)m * ldc + n) * 4) = v;
+          }
+        }
+      }
+    }
+  }
+
+  static __device__ __forceinline__ void run(__bf16* smem, const GemmParams& p, int ltid, int lane, int wm, int wn) {
     const __bf16* A = (const __bf16*)p.a;
     const __bf16* B = (const __bf16*)p.b;
     const int lda = (int)p.lda, ldb = (int)p.ldb;
+    const UnitMap um = {p.tiles_m, p.tiles_n, p.group_m, p.splits, p.kt_per_split, p.kt_total,
+                        p.tiles_m * p.tiles_n * p.splits};
+    const int stride = gridDim.x;
     OpA opa;
     OpB opb;
     if (DO_A) opa.init(ltid, lda);
     if (DO_B) opb.init(ltid, ldb);
+
+    f32x16 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
     // fragment read offsets (elements) for this lane: row part and chunk part
     const int lr = lane & 31, lh = lane >> 5;
@@ -207,67 +304,104 @@ struct FastMainLoop {
     for (int s = 0; s < 4; ++s) koff[s] = ((2 * s + lh) ^ sw) << 3;
 
     bf16x8 fa[2][FM], fb[2][FN];
-    auto read_frags = [&](const __bf16* stage, int s, int buf) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i) fa[buf][i] = as_bf16x8(*(const u32x4*)(stage + a_row[i] + koff[s]));
-#pragma unroll
-      for (int j = 0; j < FN; ++j) fb[buf][j] = as_bf16x8(*(const u32x4*)(stage + b_row[j] + koff[s]));
-    };
-    auto mfmas = [&](int buf, int i_begin, int i_end) {
-#pragma unroll
-      for (int i = i_begin; i < i_end; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(fa[buf][i], fb[buf][j], acc[i][j]);
-    };
-    auto load = [&](int k) {
-      if (DO_A) opa.load(tile_rsrc<A_KMAJ>(A, lda, row0, p.M, k, p.K));
-      if (DO_B) opb.load(tile_rsrc<B_KMAJ>(B, ldb, col0, p.N, k, p.K));
+    // fragments of k-step S (0..3) of a stage into buffer BUF
+#define DPG_READ_FRAGS(stage, S, BUF)                                                                      \
+  do {                                                                                                     \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) fa[BUF][i] =                                            \
+        as_bf16x8(*(const u32x4*)((stage) + a_row[i] + koff[S]));                                         \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) fb[BUF][j] =                                            \
+        as_bf16x8(*(const u32x4*)((stage) + b_row[j] + koff[S]));                                         \
+  } while (0)
+    // MFMAs of rows [I0, I1) of the wave tile from fragment buffer BUF
+#define DPG_MFMAS(BUF, I0, I1)                                                                             \
+  do {                                                                                                     \
+    _Pragma("unroll") for (int i = (I0); i < (I1); ++i) _Pragma("unroll") for (int j = 0; j < FN; ++j)     \
+        acc[i][j] = mfma32(fb[BUF][j], fa[BUF][i], acc[i][j]);                                             \
+  } while (0)
+    // loads of the step at cursor L (out-of-range steps read nothing)
+    auto load = [&](const StepCursor& L) {
+      // a step past the last unit gets empty descriptors (one row, no K left)
+      const bool ok = cursor_valid(um, L);
+      const int kk = ok ? (L.kt0 + L.kt) * BK : p.K;
+      if (DO_A) opa.load(tile_rsrc<A_KMAJ>(A, lda, L.row0, ok ? p.M : L.row0 + 1, kk, p.K));
+      if (DO_B) opb.load(tile_rsrc<B_KMAJ>(B, ldb, L.col0, ok ? p.N : L.col0 + 1, kk, p.K));
     };
     auto store = [&](__bf16* stage) {
       if (DO_A) opa.store(stage);
       if (DO_B) opb.store(stage + PLANE_A);
     };
 
-    if (nkt > 0) {
-      load(kt0 * BK);
-      store(smem);
-      load((kt0 + 1) * BK);
-      __syncthreads();
-      read_frags(smem, 0, 0);
-    }
+    StepCursor C = cursor_at<BM, BN>(um, blockIdx.x);
+    if (!cursor_valid(um, C)) return;
+    StepCursor L = C;
+    load(L);
+    L = cursor_next<BM, BN>(um, L, stride);
+    store(smem);
+    load(L);
+    L = cursor_next<BM, BN>(um, L, stride);
+    __syncthreads();
+    DPG_READ_FRAGS(smem, 0, 0);
 
     constexpr int NM = FM * FN;  // MFMAs per k-step
     constexpr int NR = FM + FN;  // fragment reads per k-step
     constexpr int NW = (DO_A ? OpA::LOADS : 0) + (DO_B ? OpB::LOADS : 0);  // LDS writes per tile
     constexpr int NV = NW;                                                 // buffer loads per tile
-    for (int it = 0; it < nkt; ++it) {
+    for (int it = 0; cursor_valid(um, C); ++it) {
       const __bf16* cur = smem + (it & 1) * STAGE;
       __bf16* nxt = smem + ((it + 1) & 1) * STAGE;
       // k-step 0: fragments of step 1 while the MFMAs of step 0 issue
-      read_frags(cur, 1, 1);
-      mfmas(0, 0, FM);
+      DPG_READ_FRAGS(cur, 1, 1);
+      DPG_MFMAS(0, 0, FM);
       sched_step<NM, NR, 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
-      // k-step 1: fragments of step 2; stage the next tile into the other buffer
-      read_frags(cur, 2, 0);
-      mfmas(1, 0, FM);
-      store(nxt);
-      sched_step<NM, NR, NW, 0>();
+      // k-step 1: fragments of step 2.  Waves that stage A (or both operands)
+      // write the next K tile into the other buffer and fetch the one after
+      // next here; waves that stage B do it in k-step 2, so the two waves
+      // sharing a SIMD wait for memory at different times and one of them can
+      // always issue MFMAs.
+      DPG_READ_FRAGS(cur, 2, 0);
+      DPG_MFMAS(1, 0, FM);
+      if constexpr (ROLE != ROLE_B) {
+        store(nxt);
+        load(L);
+        sched_step<NM, NR, NW, NV>();
+      } else {
+        sched_step<NM, NR, 0, 0>();
+      }
       __builtin_amdgcn_sched_barrier(0);
-      // k-step 2: fragments of step 3; fetch the tile after next
-      read_frags(cur, 3, 1);
-      mfmas(0, 0, FM);
-      load((kt0 + it + 2) * BK);
-      sched_step<NM, NR, 0, NV>();
+      // k-step 2: fragments of step 3
+      DPG_READ_FRAGS(cur, 3, 1);
+      DPG_MFMAS(0, 0, FM);
+      if constexpr (ROLE == ROLE_B) {
+        store(nxt);
+        load(L);
+        sched_step<NM, NR, NW, NV>();
+      } else {
+        sched_step<NM, NR, 0, 0>();
+      }
       __builtin_amdgcn_sched_barrier(0);
-      // k-step 3: half the MFMAs, barrier, first fragments of the next tile, rest
-      mfmas(1, 0, FM / 2);
+      // k-step 3: half the MFMAs, barrier, first fragments of the next K tile, rest
+      DPG_MFMAS(1, 0, FM / 2);
       __syncthreads();
-      read_frags(nxt, 0, 0);  // unused after the last tile (in-bounds LDS)
-      mfmas(1, FM / 2, FM);
+      DPG_READ_FRAGS(nxt, 0, 0);  // garbage after the last step (in-bounds LDS)
+      DPG_MFMAS(1, FM / 2, FM);
       sched_step<NM / 2, NR, 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
+      L = cursor_next<BM, BN>(um, L, stride);
+      if (C.kt + 1 >= C.nkt) {
+        // the unit is complete: write it while the next unit's loads are in flight
+        epilogue(p, C, lane, wm, wn, acc);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+      }
+      C = cursor_next<BM, BN>(um, C, stride);
     }
+#undef DPG_READ_FRAGS
+#undef DPG_MFMAS
   }
 };
 
@@ -275,73 +409,19 @@ template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KMAJ, bool B_KMAJ, in
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_fast_kernel(GemmParams p) {
   constexpr int BK = 64;
   constexpr int NT = 64 * WAVES_M * WAVES_N;
-  constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
-  constexpr int FM = WM / 32, FN = WN / 32;
   static_assert(NT == 256 || NT == 512, "four or eight waves");
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (BM + BN) * BK];
-
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-
-  const int tiles = p.tiles_m * p.tiles_n;
-  const int pid = xcd_remap(blockIdx.x, tiles * p.splits);
-  const int split = pid / tiles;
-  const int t = pid % tiles;
-  const int per_group = p.group_m * p.tiles_n;
-  const int group = t / per_group;
-  const int first_m = group * p.group_m;
-  const int gsize = min(p.tiles_m - first_m, p.group_m);
-  const int tm = first_m + (t % per_group) % gsize;
-  const int tn = (t % per_group) / gsize;
-  const int row0 = tm * BM, col0 = tn * BN;
-
-  const int kt0 = split * p.kt_per_split;
-  const int kt1 = min(kt0 + p.kt_per_split, p.kt_total);
-  const int nkt = kt1 - kt0;
-
-  f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
   if constexpr (NT == 512) {
     if (wave < 4)
-      FastMainLoop<BM, BN, WAVES_M, WAVES_N, A_KMAJ, B_KMAJ, ROLE_A>::run(smem, p, tid, lane, wm, wn, row0, col0, kt0,
-                                                                           nkt, acc);
+      FastGemm<BM, BN, WAVES_M, WAVES_N, A_KMAJ, B_KMAJ, OUT, ROLE_A>::run(smem, p, tid, lane, wm, wn);
     else
-      FastMainLoop<BM, BN, WAVES_M, WAVES_N, A_KMAJ, B_KMAJ, ROLE_B>::run(smem, p, tid - 256, lane, wm, wn, row0, col0,
-                                                                           kt0, nkt, acc);
+      FastGemm<BM, BN, WAVES_M, WAVES_N, A_KMAJ, B_KMAJ, OUT, ROLE_B>::run(smem, p, tid - 256, lane, wm, wn);
   } else {
-    FastMainLoop<BM, BN, WAVES_M, WAVES_N, A_KMAJ, B_KMAJ, ROLE_BOTH>::run(smem, p, tid, lane, wm, wn, row0, col0, kt0,
-                                                                          nkt, acc);
-  }
-
-  // ---- epilogue: lane l owns column (l % 32) and rows (r/4)*8 + (l/32)*4 + r%4
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int col = col0 + wn * WN + j * 32 + (lane & 31);
-      if (col >= p.N) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = row0 + wm * WM + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        if (row >= p.M) continue;
-        const float v = acc[i][j][r];
-        if (OUT == OUT_BF16) {
-          ((unsigned short*)p.c)[(int64_t)row * p.ldc + col] = (unsigned short)bf16_bits(v);
-        } else if (OUT == OUT_F32) {
-          ((float*)p.c)[(int64_t)row * p.ldc + col] = v;
-        } else {
-          ((float*)p.c)[(int64_t)split * p.split_stride + (int64_t)row * p.ldc + col] = v;
-        }
-      }
-    }
+    FastGemm<BM, BN, WAVES_M, WAVES_N, A_KMAJ, B_KMAJ, OUT, ROLE_BOTH>::run(smem, p, tid, lane, wm, wn);
   }
 }
 

@@ -77,6 +77,31 @@ bool make_plan(const PlanKey& key, Plan* p) {
     return true;
   }
   p->kind = PLAN_GEMM;
+  if (!p->x3 && p->layout == LAYOUT_WGRAD && p->M <= 128) {
+    // skinny weight gradient: units of (64 rows of N, 64 columns of K), token splits
+    p->skinny = 1;
+    p->tile = 2;
+    p->tiles_m = (int)cdiv(p->M, 64);
+    p->tiles_n = (int)cdiv(p->N, 64);
+    p->kt_total = (int)cdiv(p->K, 64);  // 64-token blocks
+    const int64_t units = (int64_t)p->tiles_m * p->tiles_n;
+    int64_t s;
+    if (key.split_req > 0) {
+      s = key.split_req;
+    } else {
+      s = (key.cus + units / 2) / units;
+      s = std::min<int64_t>(s, std::max<int64_t>(1, p->kt_total / 16));
+    }
+    s = std::max<int64_t>(1, std::min<int64_t>(s, p->kt_total));
+    p->kt_per_split = (int)cdiv(p->kt_total, s);
+    p->splits = (int)cdiv(p->kt_total, p->kt_per_split);
+    p->group_m = 1;
+    p->grid = units * p->splits;
+    p->ws_bytes = p->splits > 1 ? (size_t)p->splits * (size_t)p->M * (size_t)p->N * 4u : 0;
+    const double bytes = 2.0 * (p->K * p->N + p->K * p->M) + (double)p->M * p->N * (p->splits > 1 ? 8.0 * p->splits : 4.0);
+    p->est_us = bytes / kHbm * 1e6 + kLaunchUs * (p->splits > 1 ? 2 : 1);
+    return p->grid <= INT32_MAX;
+  }
   const int in_bytes = p->x3 ? 4 : 2;
   const int out_bytes = key.out == 1 ? 4 : 2;
   static const int kSplitChoices[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
@@ -124,7 +149,8 @@ int describe_plan(const PlanKey& key, const Plan& p, char* buf, size_t buflen) {
                   "pass=%s kind=gemm det=%d M=%lld N=%lld K=%lld layout=%s x3=%d out=%s tile=%dx%dx%d threads=%d "
                   "kernel=%s tiles=%dx%d group_m=%d splits=%d kt_total=%d kt_per_split=%d grid=%lld workspace=%zu est_us=%.1f",
                   kPass[key.pass], key.det, (long long)p.M, (long long)p.N, (long long)p.K, kLayout[p.layout], p.x3,
-                  p.out ? "f32" : "bf16", ts.bm, ts.bn, ts.bk, ts.threads, p.fast ? "pipelined" : "generic", p.tiles_m, p.tiles_n, p.group_m, p.splits,
+                  p.out ? "f32" : "bf16", p.skinny ? 64 : ts.bm, p.skinny ? 64 : ts.bn, ts.bk, p.skinny ? 512 : ts.threads,
+                  p.skinny ? "skinny" : (p.fast ? "pipelined" : "generic"), p.tiles_m, p.tiles_n, p.group_m, p.splits,
                   p.kt_total, p.kt_per_split, (long long)p.grid, p.ws_bytes, p.est_us);
 }
 

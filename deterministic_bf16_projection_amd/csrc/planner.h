@@ -43,6 +43,7 @@ struct Plan {
   int64_t M, N, K;     // GEMM view: C[M,N] = sum_k A(m,k) B(n,k)
   int tile;            // index into kTiles
   int fast;            // software-pipelined kernel (gemm_fast.h) instead of the generic one
+  int skinny;          // streaming weight-gradient kernel for N <= 128 (skinny_wgrad.h)
   int tiles_m, tiles_n;
   int splits, kt_total, kt_per_split;
   int group_m;
