@@ -31,7 +31,8 @@ PEAK_HBM_GBPS = 8000.0
 T_BIG, N_BIG, K_BIG = 16384, 12288, 4096
 SKINNY = [(4096, 64), (4096, 128), (5120, 48), (5120, 64)]
 T_SKINNY = 16384
-KERNEL_SOURCES = ["deterministic_bf16_projection_amd/csrc/gemm_kernel.h",
+KERNEL_SOURCES = ["deterministic_bf16_projection_amd/csrc/gemm_fast.h",
+                  "deterministic_bf16_projection_amd/csrc/gemm_kernel.h",
                   "deterministic_bf16_projection_amd/csrc/device_common.h"]
 
 
@@ -46,7 +47,7 @@ def kernel_source_hash():
 def read_traffic(kernel_pass):
     """HBM bytes per launch of the dominant kernel from the committed rocprofv3
     PMC summary, if it was taken from the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "gemm_%s_4096x12288_T16384_pmc.txt" % kernel_pass)
+    path = os.path.join(PROFILE_DIR, "gemm_%s_4096x12288_T16384_pmc.txt" % kernel_pass)
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -55,6 +56,123 @@ def read_traffic(kernel_pass):
     if not m or not b or m.group(1) != kernel_source_hash():
         return None
     return float(b.group(1))
+
+
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+PASS_KERNEL_TAG = {  # template arguments (A K-major, B K-major) of each pass's GEMM kernel
+    "fwd": "true, true", "dgrad": "true, false", "wgrad": "false, false"}
+COPY_BYTES = 1 << 30
+
+
+def profile_run():
+    """One step of the three passes plus a plain 1 GiB device copy whose HBM
+    bytes are known (used to scale the FETCH_SIZE / WRITE_SIZE counters)."""
+    import numpy as np
+    import torch
+    import dpg_inputs
+    import deterministic_bf16_projection_amd as dpg
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    x, w, dy = dpg_inputs.dense(T_BIG, N_BIG, K_BIG, seed_group=0)
+    X, W, DY = to_dev(x), to_dev(w), to_dev(dy)
+    Y = dpg.dpg_forward(X, W)
+    DX = dpg.dpg_dgrad(DY, W)
+    DW = dpg.dpg_wgrad(DY, X)
+    torch.cuda.synchronize()
+    print("profile run done", Y.shape, DX.shape, DW.shape)
+
+
+def _read_counter_csv(path):
+    import csv
+    rows = list(csv.DictReader(open(path)))
+    out = []
+    for r in rows:
+        out.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]), r.get("Grid_Size")))
+    return out
+
+
+def summarize_pmc(fetch_csv, write_csv, command):
+    """Writes profiles/gemm_<pass>_4096x12288_T16384_pmc.txt from two rocprofv3
+    --pmc runs (FETCH_SIZE, WRITE_SIZE; kilobytes per dispatch)."""
+    fetch = _read_counter_csv(fetch_csv)
+    write = _read_counter_csv(write_csv)
+
+    def pick(rows, pred):
+        vals = [v for (k, c, v, g) in rows if pred(k)]
+        return vals
+
+    copy_pred = lambda k: "dpg" not in k and "copybuffer" in k.lower()
+    copy_fetch = pick(fetch, copy_pred)
+    copy_write = pick(write, copy_pred)
+    if not copy_fetch or not copy_write:
+        raise SystemExit("no copy kernel in the counter files")
+    # the largest copy dispatch is the 1 GiB calibration copy
+    f_scale = (COPY_BYTES / 1024.0) / max(copy_fetch)
+    w_scale = (COPY_BYTES / 1024.0) / max(copy_write)
+    for name, tag in PASS_KERNEL_TAG.items():
+        pred = lambda k, tag=tag: "gemm_fast_kernel<256, 256" in k and (", %s," % tag) in k
+        fk = pick(fetch, pred)
+        wk = pick(write, pred)
+        if not fk or not wk:
+            continue
+        fetch_b = fk[-1] * 1024.0 * f_scale
+        write_b = wk[-1] * 1024.0 * w_scale
+        alg = 2.0 * (T_BIG * K_BIG + N_BIG * K_BIG) if name == "fwd" else (
+            2.0 * (T_BIG * N_BIG + N_BIG * K_BIG) if name == "dgrad" else 2.0 * (T_BIG * N_BIG + T_BIG * K_BIG))
+        out_b = 2.0 * {"fwd": T_BIG * N_BIG, "dgrad": T_BIG * K_BIG, "wgrad": N_BIG * K_BIG}[name]
+        path = os.path.join(PROFILE_DIR, "gemm_%s_4096x12288_T16384_pmc.txt" % name)
+        with open(path, "w") as f:
+            f.write("HBM traffic of the %s GEMM kernel (4096->12288, T=16384, BF16 out), rocprofv3 PMC on MI355X\n" % name)
+            f.write("commands:\n  %s\n" % command.replace("\n", "\n  "))
+            f.write("kernel_source_hash: %s\n" % kernel_source_hash())
+            f.write("calibration: 1 GiB device copy read %.1f KB / wrote %.1f KB -> scale fetch x%.4f, write x%.4f\n"
+                    % (max(copy_fetch), max(copy_write), f_scale, w_scale))
+            f.write("FETCH_SIZE raw: %.1f KB   WRITE_SIZE raw: %.1f KB\n" % (fk[-1], wk[-1]))
+            f.write("fetch_bytes_per_launch: %.4g\nwrite_bytes_per_launch: %.4g\n" % (fetch_b, write_b))
+            f.write("hbm_bytes_per_launch: %.4g\n" % (fetch_b + write_b))
+            f.write("algorithmic bytes (operands once + output): %.4g (ratio %.2f)\n"
+                    % (alg + out_b, (fetch_b + write_b) / (alg + out_b)))
+        print("wrote", path)
+
+
+def summarize_trace(stats_csv, command, out_name="bench_4096x12288_T16384_kernel_trace.txt"):
+    """Writes the kernel-trace summary (rocprofv3 --stats) under profiles/."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    path = os.path.join(PROFILE_DIR, out_name)
+    with open(path, "w") as f:
+        f.write("rocprofv3 kernel trace of bench.py on MI355X (gfx950)\n")
+        f.write("command: %s\n" % command)
+        f.write("kernel_source_hash: %s\n\n" % kernel_source_hash())
+        f.write("%6s %10s %12s %8s  %s\n" % ("calls", "avg_us", "total_us", "pct", "kernel"))
+        for r in rows:
+            name = r["Name"].replace("void ", "").replace("(dpg::GemmParams)", "").replace("dpg::", "")
+            f.write("%6s %10.1f %12.1f %8.2f  %s\n" % (r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                      float(r["TotalDurationNs"]) / 1e3, float(r["Percentage"]),
+                                                      name[:150]))
+        trace_csv = os.path.join(os.path.dirname(stats_csv), os.path.basename(stats_csv).replace(
+            "kernel_stats", "kernel_trace"))
+        if os.path.exists(trace_csv):
+            per = {}
+            for r in csv.DictReader(open(trace_csv)):
+                if "gemm_fast_kernel<256, 256" in r["Kernel_Name"]:
+                    per.setdefault(r["Kernel_Name"], []).append(
+                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            f.write("\nlast 5 dispatches (the timed steps; the first ones are warmups):\n")
+            for k, v in per.items():
+                last = v[-5:]
+                f.write("  %10.1f us avg  %s\n" % (sum(last) / len(last), k.replace("void ", "")[:90]))
+        f.write("\ngemm_fast_kernel<256, 256, 2, 4, A K-major, B K-major, OUT>: forward = <true, true>, "
+                "input gradient = <true, false>, weight gradient = <false, false>; 1.649e12 FLOP per launch.\n"
+                "skinny_wgrad_kernel and splitk_reduce_kernel: the skinny-N weight gradients (T=16384).\n")
+    print("wrote", path)
 
 
 def cpu_baseline(target_s=12.0):
@@ -87,11 +205,24 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-skinny", action="store_true")
+    ap.add_argument("--profile-run", action="store_true", help="one step + a 1 GiB calibration copy (for rocprofv3)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"))
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "COMMAND"))
     args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.profile_run:
+        profile_run()
+        return
 
     import numpy as np
     import torch
@@ -149,7 +280,7 @@ def main():
     dominant = max(per_pass, key=lambda k: per_pass[k]["us_mean"])
     achieved = flop_pass / (per_pass[dominant]["us_mean"] * 1e-6) / 1e12
     traffic = read_traffic(dominant)
-    roofline = {"bound": "mfma", "kernel": "gemm_kernel (%s, 256x256x64 tile)" % dominant,
+    roofline = {"bound": "mfma", "kernel": "gemm_fast_kernel (%s pass, 256x256x64 tile)" % dominant,
                 "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "algorithmic_flop_per_launch": flop_pass}

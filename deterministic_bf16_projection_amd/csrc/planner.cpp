@@ -149,7 +149,8 @@ int describe_plan(const PlanKey& key, const Plan& p, char* buf, size_t buflen) {
                   "pass=%s kind=gemm det=%d M=%lld N=%lld K=%lld layout=%s x3=%d out=%s tile=%dx%dx%d threads=%d "
                   "kernel=%s tiles=%dx%d group_m=%d splits=%d kt_total=%d kt_per_split=%d grid=%lld workspace=%zu est_us=%.1f",
                   kPass[key.pass], key.det, (long long)p.M, (long long)p.N, (long long)p.K, kLayout[p.layout], p.x3,
-                  p.out ? "f32" : "bf16", p.skinny ? 64 : ts.bm, p.skinny ? 64 : ts.bn, ts.bk, p.skinny ? 512 : ts.threads,
+                  p.out ? "f32" : "bf16", p.skinny ? 64 : ts.bm, p.skinny ? 64 : ts.bn, ts.bk,
+                  (p.skinny || (p.fast && p.tile == 0)) ? 512 : ts.threads,
                   p.skinny ? "skinny" : (p.fast ? "pipelined" : "generic"), p.tiles_m, p.tiles_n, p.group_m, p.splits,
                   p.kt_total, p.kt_per_split, (long long)p.grid, p.ws_bytes, p.est_us);
 }
