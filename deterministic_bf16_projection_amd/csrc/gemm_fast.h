@@ -23,6 +23,7 @@
 #include "device_common.h"
 #include "gemm_kernel.h"
 
+
 namespace dpg {
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;

@@ -9,9 +9,10 @@
 namespace dpg {
 
 const TileShape kTiles[kNumTiles] = {
-    {256, 256, 64, 256, 1, 1.00, false, true},
-    {128, 128, 64, 256, 1, 0.80, true, true},
-    {64, 64, 64, 256, 2, 0.45, true, false},
+    // bm, bn, bk, threads, occupancy, eff (sustained fraction of the CU MFMA rate), x3_ok, fast_ok
+    {256, 256, 64, 256, 1, 0.50, false, true},
+    {128, 128, 64, 256, 2, 0.36, true, true},
+    {64, 64, 64, 256, 4, 0.20, true, false},
 };
 
 namespace {
@@ -37,6 +38,10 @@ void gemm_view(int pass, int64_t T, int64_t N, int64_t K, int64_t* m, int64_t* n
   }
 }
 
+// Time model of one plan (microseconds).  The units (tile x split) run on
+// cus * occupancy workgroup slots in waves; a CU holding fewer workgroups than
+// its occupancy runs them at a proportionally lower rate.  Memory: operands
+// once, the output, and the split partials written and read back.
 double estimate_us(const TileShape& ts, int64_t M, int64_t N, int64_t K, int x3, int out_bytes, int in_bytes,
                    int splits_req, int cus, int* splits_out, int* kt_per_out) {
   const int64_t tiles = cdiv(M, ts.bm) * cdiv(N, ts.bn);
@@ -44,14 +49,17 @@ double estimate_us(const TileShape& ts, int64_t M, int64_t N, int64_t K, int x3,
   int64_t s = std::min<int64_t>(splits_req, kt_total);
   const int64_t kt_per = cdiv(kt_total, s);
   s = cdiv(kt_total, kt_per);  // no empty splits
-  const int64_t wgs = tiles * s;
-  const double flop_wg = 2.0 * ts.bm * ts.bn * (double)(kt_per * ts.bk) * (x3 ? 3 : 1);
-  const int64_t per_cu = cdiv(wgs, cus);
-  const double t_mfma = per_cu * flop_wg / (kCuFlops * ts.eff);
-  const double bytes = (double)(M * K + N * K) * in_bytes + (double)M * N * (s > 1 ? 4.0 * s : out_bytes);
+  const int64_t units = tiles * s;
+  const double flop_unit = 2.0 * ts.bm * ts.bn * (double)(kt_per * ts.bk) * (x3 ? 3 : 1);
+  const int64_t occ_used = std::min<int64_t>(ts.occupancy, cdiv(units, cus));
+  const int64_t rounds = cdiv(units, (int64_t)cus * occ_used);
+  const double cu_rate = kCuFlops * ts.eff * (double)occ_used / ts.occupancy;  // whole CU
+  const double t_mfma = rounds * occ_used * flop_unit / cu_rate;
+  const double bytes = (double)(M * K + N * K) * in_bytes + (double)M * N * out_bytes;
   const double t_mem = bytes / kHbm;
   double t = std::max(t_mfma, t_mem) * 1e6 + kLaunchUs;
-  if (s > 1) t += ((double)M * N * (4.0 * s + out_bytes)) / kHbm * 1e6 + kLaunchUs;
+  // split partials: written by the GEMM, read back by the reduce kernel (not hidden)
+  if (s > 1) t += (double)M * N * 4.0 * (s + 1) / kHbm * 1e6 + kLaunchUs;
   *splits_out = (int)s;
   *kt_per_out = (int)kt_per;
   return t;
@@ -113,7 +121,7 @@ bool make_plan(const PlanKey& key, Plan* p) {
       if (key.split_req != 0 && sc != key.split_req) continue;
       int s, ktp;
       const double t = estimate_us(ts, p->M, p->N, p->K, p->x3, out_bytes, in_bytes, sc, key.cus, &s, &ktp);
-      if (t < best * 0.999) {  // prefer the earlier (larger tile, fewer splits) choice on near ties
+      if (t < best * 0.97) {  // prefer the earlier (larger tile, fewer splits) choice unless 3% faster
         best = t;
         p->tile = ti;
         p->splits = s;
