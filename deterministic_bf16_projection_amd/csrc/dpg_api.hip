@@ -236,25 +236,29 @@ dpg_status run(int pass, const void* a, int64_t lda, const void* b, int64_t ldb,
     q.T = (int)plan.K;
     q.N = (int)plan.M;
     q.K = (int)plan.N;
-    q.n_blocks = plan.tiles_m;
-    q.k_blocks = plan.tiles_n;
+    q.k_blocks = (int)((plan.N + 127) / 128);
     q.splits = plan.splits;
     q.tb_total = plan.kt_total;
     q.tb_per_split = plan.kt_per_split;
+    const bool wide = plan.M > 64;  // two 64-row blocks of dW per unit
     const void* kfn;
     if (plan.splits > 1) {
       q.out = ws;
       q.ldo = plan.N;
       q.split_stride = plan.M * plan.N;
-      kfn = (const void*)&skinny_wgrad_kernel<OUT_PARTIAL>;
+      kfn = wide ? (const void*)&skinny_wgrad_kernel<2, OUT_PARTIAL> : (const void*)&skinny_wgrad_kernel<1, OUT_PARTIAL>;
     } else {
       q.out = c;
       q.ldo = ldc;
       q.split_stride = 0;
-      kfn = out == DPG_BF16 ? (const void*)&skinny_wgrad_kernel<OUT_BF16> : (const void*)&skinny_wgrad_kernel<OUT_F32>;
+      if (out == DPG_BF16)
+        kfn = wide ? (const void*)&skinny_wgrad_kernel<2, OUT_BF16> : (const void*)&skinny_wgrad_kernel<1, OUT_BF16>;
+      else
+        kfn = wide ? (const void*)&skinny_wgrad_kernel<2, OUT_F32> : (const void*)&skinny_wgrad_kernel<1, OUT_F32>;
     }
     void* sargs[] = {&q};
-    hipError_t e = hipLaunchKernel(kfn, dim3((unsigned)plan.grid), dim3(512), sargs, 0, stream);
+    const unsigned sgrid = (unsigned)q.k_blocks * (unsigned)plan.splits;
+    hipError_t e = hipLaunchKernel(kfn, dim3(sgrid), dim3(512), sargs, 0, stream);
     if (e != hipSuccess) return DPG_ERR_HIP;
     if (plan.splits > 1) return launch_reduce(plan, ws, c, ldc, out, stream);
     return DPG_OK;

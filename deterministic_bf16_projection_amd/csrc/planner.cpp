@@ -86,13 +86,15 @@ bool make_plan(const PlanKey& key, Plan* p) {
   }
   p->kind = PLAN_GEMM;
   if (!p->x3 && p->layout == LAYOUT_WGRAD && p->M <= 128) {
-    // skinny weight gradient: units of (64 rows of N, 64 columns of K), token splits
+    // skinny weight gradient: units of (all N rows, 128 columns of K, token
+    // split); tiles_m / tiles_n keep the 64x64 tile counts of the generic
+    // kernel, which runs the plan when a leading dimension is too large
     p->skinny = 1;
     p->tile = 2;
     p->tiles_m = (int)cdiv(p->M, 64);
     p->tiles_n = (int)cdiv(p->N, 64);
     p->kt_total = (int)cdiv(p->K, 64);  // 64-token blocks
-    const int64_t units = (int64_t)p->tiles_m * p->tiles_n;
+    const int64_t units = cdiv(p->N, 128);
     int64_t s;
     if (key.split_req > 0) {
       s = key.split_req;
@@ -104,7 +106,7 @@ bool make_plan(const PlanKey& key, Plan* p) {
     p->kt_per_split = (int)cdiv(p->kt_total, s);
     p->splits = (int)cdiv(p->kt_total, p->kt_per_split);
     p->group_m = 1;
-    p->grid = units * p->splits;
+    p->grid = (int64_t)p->tiles_m * p->tiles_n * p->splits;  // generic-kernel grid
     p->ws_bytes = p->splits > 1 ? (size_t)p->splits * (size_t)p->M * (size_t)p->N * 4u : 0;
     const double bytes = 2.0 * (p->K * p->N + p->K * p->M) + (double)p->M * p->N * (p->splits > 1 ? 8.0 * p->splits : 4.0);
     p->est_us = bytes / kHbm * 1e6 + kLaunchUs * (p->splits > 1 ? 2 : 1);
