@@ -48,72 +48,90 @@ __device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[
   }
 }
 
+// The same transpose with the byte selectors of even and odd output slots
+// passed in: swapping them (a per-lane choice) puts column m ^ 1 in slot m.
+__device__ __forceinline__ void transpose8x8_sel(const u32x4 (&in)[8], u32x4 (&out)[8], uint32_t sel_even,
+                                                 uint32_t sel_odd) {
+#pragma unroll
+  for (int m = 0; m < 8; ++m) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      out[m][e] = __builtin_amdgcn_perm(in[2 * e + 1][m >> 1], in[2 * e][m >> 1], (m & 1) ? sel_odd : sel_even);
+  }
+}
+
 // LDS K-major layout: row r (64 BF16 = 8 chunks of 16 B); chunk c stored at
-// position c ^ swz(r).  Rows r and r + 8 use different patterns so that the
-// 16 rows one ds_read_b128 phase may touch fall on distinct banks.
-__device__ __forceinline__ int fswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+// position c ^ fswz(r), a 3-bit pattern of r and r / 8.  The 16 rows one
+// ds_read_b128 phase touches (16 consecutive rows) fall on distinct banks, and
+// so do the rows 8 mb + m of a transposed-block write phase (see FastOperand).
+// For a row 32 q + l (l < 32), fswz = fswz(l) ^ 4 (q & 1).
+__device__ __forceinline__ int fswz(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int lds_chunk_off(int r, int c) { return r * 64 + ((c ^ fswz(r)) << 3); }
 
 // One operand: R rows (M or N side) by 64 reduction elements per K tile.
 template <int R, bool KMAJ, int NT>
 struct FastOperand {
-  // K-major: 16-byte chunks (row, k-chunk) per thread, rows tid/8 + (NT/8) i.
-  // MN-major: one 8x8 block per thread for the first R threads (R <= NT), or
-  // R/NT blocks per thread.
-  static constexpr int LOADS = KMAJ ? R * 8 / NT : (R >= NT ? R * 8 / NT : 8);
-  static constexpr int BLOCK_THREADS = KMAJ ? NT : (R >= NT ? NT : R);  // threads that own data
+  // K-major: 16-byte chunks (row, k-chunk) per thread, rows tid/8 + 32 i.
+  // MN-major: one 8x8 block per thread for the first R threads.
+  static_assert(NT == 256 && (KMAJ || R <= NT), "one block per thread, 32 rows per K-major load");
+  static constexpr int LOADS = KMAJ ? R * 8 / NT : 8;
+  static constexpr int BLOCK_THREADS = KMAJ ? NT : R;  // threads that own data
   u32x4 g[LOADS];
-  uint32_t voff[LOADS];
-  int lds_off[LOADS];  // element offsets within one operand plane
+  // Load i reads at voff0 + i * vstep bytes, and LDS slot i goes to lds0 with
+  // a per-slot constant (added for K-major, XORed for MN-major).
+  uint32_t voff0, vstep;
+  int lds0;
+  uint32_t sel_even, sel_odd;  // transpose byte selectors (MN-major)
   bool owner;
 
   // set up per-thread offsets; ld in elements
   __device__ __forceinline__ void init(int tid, int64_t ld) {
     owner = tid < BLOCK_THREADS;
     if (KMAJ) {
-      const int c = tid & 7;
-#pragma unroll
-      for (int i = 0; i < LOADS; ++i) {
-        const int r = (tid >> 3) + (NT / 8) * i;
-        voff[i] = (uint32_t)(r * ld * 2 + c * 16);
-        lds_off[i] = lds_chunk_off(r, c);
-      }
+      // rows r + 32 i: offset lds_chunk_off(r, c) + 2048 i, with chunk bit 2
+      // flipped for odd i (fswz(r + 32) = fswz(r) ^ 4)
+      const int c = tid & 7, r = tid >> 3;
+      voff0 = (uint32_t)(r * ld * 2 + c * 16);
+      vstep = (uint32_t)(32 * ld * 2);
+      lds0 = lds_chunk_off(r, c);
     } else {
-      // block: kc = tid & 7 (which 8 reduction rows), mb = tid >> 3 (+32 per block)
-      const int kc = tid & 7;
-#pragma unroll
-      for (int b = 0; b < LOADS / 8; ++b) {
-        const int mb = (tid >> 3) + (NT / 8) * b;
-#pragma unroll
-        for (int l = 0; l < 8; ++l) {
-          voff[b * 8 + l] = (uint32_t)((kc * 8 + l) * ld * 2 + mb * 16);
-          lds_off[b * 8 + l] = lds_chunk_off(mb * 8 + l, kc);
-        }
-      }
+      // mb = tid % (R/8) (8 columns), kc = tid / (R/8) (8 reduction rows), so
+      // consecutive lanes read consecutive 16-byte chunks of one row.  Lanes
+      // with (mb / 8) odd keep column m ^ 1 in slot m: the 16 lanes of a write
+      // phase then cover rows of both parities and, with the row swizzle, 16
+      // distinct bank groups.  Slot m goes to row 8 mb + (m ^ flip), i.e. to
+      // element offset lds0 ^ 72 m with lds0 = 512 mb | 8 (9 flip ^ (kc ^ mb) % 8).
+      const int mb = tid % (R / 8), kc = (tid / (R / 8)) & 7;
+      const int flip = (mb >> 3) & 1;
+      sel_even = flip ? 0x07060302u : 0x05040100u;
+      sel_odd = flip ? 0x05040100u : 0x07060302u;
+      voff0 = (uint32_t)(kc * 8 * ld * 2 + mb * 16);
+      vstep = (uint32_t)(ld * 2);
+      lds0 = (mb * 512) | ((((9 * flip) ^ ((kc ^ mb) & 7))) << 3);
     }
   }
 
   __device__ __forceinline__ void load(rsrc_t r) {
     if (BLOCK_THREADS < NT && !owner) return;
+    const uint32_t v = voff0;
 #pragma unroll
-    for (int i = 0; i < LOADS; ++i) g[i] = buf_load16(r, voff[i]);
+    for (int i = 0; i < LOADS; ++i) g[i] = buf_load16(r, v + (uint32_t)i * vstep);
   }
 
   __device__ __forceinline__ void store(__bf16* plane) const {
     if (BLOCK_THREADS < NT && !owner) return;
-    if (KMAJ) {
+    int o = lds0;
+    // MN-major: form the eight slot offsets here rather than in the loop
+    // preheader (the eight-wave kernels would otherwise run out of registers)
+    if constexpr (!KMAJ) asm volatile("" : "+v"(o));
+    if constexpr (KMAJ) {
 #pragma unroll
-      for (int i = 0; i < LOADS; ++i) *(u32x4*)(plane + lds_off[i]) = g[i];
+      for (int i = 0; i < LOADS; ++i) *(u32x4*)(plane + ((i & 1) ? (o ^ 32) : o) + 2048 * i) = g[i];
     } else {
+      u32x4 out[8];
+      transpose8x8_sel(g, out, sel_even, sel_odd);
 #pragma unroll
-      for (int b = 0; b < LOADS / 8; ++b) {
-        u32x4 in[8], out[8];
-#pragma unroll
-        for (int l = 0; l < 8; ++l) in[l] = g[b * 8 + l];
-        transpose8x8(in, out);
-#pragma unroll
-        for (int m = 0; m < 8; ++m) *(u32x4*)(plane + lds_off[b * 8 + m]) = out[m];
-      }
+      for (int m = 0; m < 8; ++m) *(u32x4*)(plane + (o ^ (72 * m))) = out[m];
     }
   }
 };
@@ -231,6 +249,7 @@ struct FastGemm {
   static constexpr int NT = 64 * WAVES_M * WAVES_N;
   static constexpr int NTL = ROLE == ROLE_BOTH ? NT : NT / 2;  // threads staging one operand
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static_assert(WM % 64 == 0 && WN % 64 == 0, "fragment swizzle parity follows the fragment index");
   static constexpr int FM = WM / 32, FN = WN / 32;
   static constexpr int PLANE_A = BM * BK, PLANE_B = BN * BK, STAGE = PLANE_A + PLANE_B;
   typedef FastOperand<BM, A_KMAJ, NTL> OpA;
@@ -294,7 +313,10 @@ struct FastGemm {
 
     // fragment read offsets (elements) for this lane: row part and chunk part
     const int lr = lane & 31, lh = lane >> 5;
-    const int sw = fswz(lr);  // rows of a fragment start at multiples of 32
+    // fragment rows start at multiples of 32 (wave tiles at multiples of 64):
+    // fragment i sits at pattern fswz(lr) ^ 4 (i & 1), so it reads chunk
+    // (2 S + lh) at koff[S ^ 2 (i & 1)]
+    const int sw = fswz(lr);
     int a_row[FM], b_row[FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) a_row[i] = (wm * WM + i * 32 + lr) * 64;
@@ -309,9 +331,9 @@ struct FastGemm {
 #define DPG_READ_FRAGS(stage, S, BUF)                                                                      \
   do {                                                                                                     \
     _Pragma("unroll") for (int i = 0; i < FM; ++i) fa[BUF][i] =                                            \
-        as_bf16x8(*(const u32x4*)((stage) + a_row[i] + koff[S]));                                         \
+        as_bf16x8(*(const u32x4*)((stage) + a_row[i] + koff[(S) ^ (2 * (i & 1))]));                       \
     _Pragma("unroll") for (int j = 0; j < FN; ++j) fb[BUF][j] =                                            \
-        as_bf16x8(*(const u32x4*)((stage) + b_row[j] + koff[S]));                                         \
+        as_bf16x8(*(const u32x4*)((stage) + b_row[j] + koff[(S) ^ (2 * (j & 1))]));                       \
   } while (0)
     // MFMAs of rows [I0, I1) of the wave tile from fragment buffer BUF
 #define DPG_MFMAS(BUF, I0, I1)                                                                             \

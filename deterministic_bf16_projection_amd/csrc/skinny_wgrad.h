@@ -65,21 +65,29 @@ __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
 
   // Staging: X tile (cb, g) is shared by the NB waves (*, cb, g) and dY tile
   // (nb, g) by the CB waves (nb, *, g).  A tile is 8 x 8 sub-blocks of 8x8; lane
-  // (kc, sb) of a wave owns token rows kc*8.. and columns sb*8.., and each of a
-  // tile's sharers fetches an equal range of column sub-blocks.
-  const int kc = lane & 7, sb = lane >> 3;
-  const bool x_lane = sb / (8 / NB) == nb;
-  const bool y_lane = sb / (8 / CB) == cb;
+  // (kc, sb) = (lane / 8, lane % 8) owns token rows kc*8.. and columns sb*8.., so
+  // the 8 lanes of one token row read 128 contiguous bytes; each of a tile's
+  // sharers fetches an equal range of token rows.
+  const int kc = lane >> 3, sb = lane & 7;
+  const bool x_lane = kc / (8 / NB) == nb;
+  const bool y_lane = kc / (8 / CB) == cb;
+  // Lanes with odd kc hold transposed column m ^ 1 in slot m (a per-lane choice
+  // of byte selectors), so that the 16 lanes of one LDS write phase cover rows of
+  // both parities; with the row swizzle the writes are then conflict-free.
+  const int odd = kc & 1;
+  const uint32_t sel_even = odd ? 0x07060302u : 0x05040100u;
+  const uint32_t sel_odd = odd ? 0x05040100u : 0x07060302u;
   uint32_t voff_x[8], voff_y[8];
   int lds_off[8];
 #pragma unroll
   for (int l = 0; l < 8; ++l) {
     voff_x[l] = (uint32_t)(((kc * 8 + l) * ldx + cb * 64 + sb * 8) * 2);
     voff_y[l] = (uint32_t)(((kc * 8 + l) * lddy + nb * 64 + sb * 8) * 2);
-    lds_off[l] = lds_chunk_off(sb * 8 + l, kc);
+    const int row = sb * 8 + (l ^ odd);
+    lds_off[l] = lds_chunk_off(row, kc);
   }
-  __bf16* x_tile = smem + (g * CB + cb) * TILE;                  // shared with the NB waves (cb, g)
-  __bf16* y_tile = smem + (X_TILES + g * NB + nb) * TILE;        // shared with the CB waves (nb, g)
+  __bf16* x_tile = smem + (g * CB + cb) * TILE;            // shared with the NB waves (*, cb, g)
+  __bf16* y_tile = smem + (X_TILES + g * NB + nb) * TILE;  // shared with the CB waves (nb, *, g)
 
   auto rsrc_rows = [&](const __bf16* base, int ld, int col0, int cols, int t0) {
     const int rows = min(p.T - t0, 64);
@@ -97,6 +105,8 @@ __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
+  // fragment rows i*32 + lr: fswz(i*32 + lr) = fswz(lr) ^ 4i, i.e. chunk
+  // (2s + lh) of fragment 1 sits where chunk (2(s^2) + lh) of fragment 0 does
   const int lr = lane & 31, lh = lane >> 5;
   const int sw = fswz(lr);
   int koff[4];
@@ -121,12 +131,12 @@ __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
   auto stage = [&]() {
     u32x4 t[8];
     if (x_lane) {
-      transpose8x8(gx, t);
+      transpose8x8_sel(gx, t, sel_even, sel_odd);
 #pragma unroll
       for (int m = 0; m < 8; ++m) *(u32x4*)(x_tile + lds_off[m]) = t[m];
     }
     if (y_lane) {
-      transpose8x8(gy, t);
+      transpose8x8_sel(gy, t, sel_even, sel_odd);
 #pragma unroll
       for (int m = 0; m < 8; ++m) *(u32x4*)(y_tile + lds_off[m]) = t[m];
     }
@@ -141,9 +151,9 @@ __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
     for (int s = 0; s < 4; ++s) {
       bf16x8 fa[2], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i) fa[i] = as_bf16x8(*(const u32x4*)(y_tile + (i * 32 + lr) * 64 + koff[s]));
+      for (int i = 0; i < 2; ++i) fa[i] = as_bf16x8(*(const u32x4*)(y_tile + (i * 32 + lr) * 64 + koff[s ^ (2 * i)]));
 #pragma unroll
-      for (int j = 0; j < 2; ++j) fb[j] = as_bf16x8(*(const u32x4*)(x_tile + (j * 32 + lr) * 64 + koff[s]));
+      for (int j = 0; j < 2; ++j) fb[j] = as_bf16x8(*(const u32x4*)(x_tile + (j * 32 + lr) * 64 + koff[s ^ (2 * j)]));
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
