@@ -77,6 +77,25 @@ KernelFn lookup_fast_kernel(int tile, int layout, int out_kind) {
   return table[tile][layout][out_kind];
 }
 
+// skinny weight-gradient kernels: (64-row blocks NB, 64-column blocks CB, out kind)
+typedef void (*SkinnyFn)(SkinnyParams);
+template <int NB, int CB>
+struct SkinnyRow {
+  static constexpr SkinnyFn fns[3] = {&skinny_wgrad_kernel<NB, CB, OUT_BF16>, &skinny_wgrad_kernel<NB, CB, OUT_F32>,
+                                      &skinny_wgrad_kernel<NB, CB, OUT_PARTIAL>};
+};
+
+SkinnyFn lookup_skinny_kernel(int nb, int cb, int out_kind) {
+  static const SkinnyFn table[2][2][3] = {
+      {{SkinnyRow<1, 1>::fns[0], SkinnyRow<1, 1>::fns[1], SkinnyRow<1, 1>::fns[2]},
+       {SkinnyRow<1, 2>::fns[0], SkinnyRow<1, 2>::fns[1], SkinnyRow<1, 2>::fns[2]}},
+      {{SkinnyRow<2, 1>::fns[0], SkinnyRow<2, 1>::fns[1], SkinnyRow<2, 1>::fns[2]},
+       {SkinnyRow<2, 2>::fns[0], SkinnyRow<2, 2>::fns[1], SkinnyRow<2, 2>::fns[2]}},
+  };
+  if (nb < 1 || nb > 2 || cb < 1 || cb > 2 || out_kind < 0 || out_kind > 2) return nullptr;
+  return table[nb - 1][cb - 1][out_kind];
+}
+
 int tile_threads(int tile) { return kTiles[tile].threads; }
 
 // ----------------------------------------------------------- plan cache --
@@ -236,29 +255,26 @@ dpg_status run(int pass, const void* a, int64_t lda, const void* b, int64_t ldb,
     q.T = (int)plan.K;
     q.N = (int)plan.M;
     q.K = (int)plan.N;
-    q.k_blocks = (int)((plan.N + 127) / 128);
     q.splits = plan.splits;
     q.tb_total = plan.kt_total;
     q.tb_per_split = plan.kt_per_split;
-    const bool wide = plan.M > 64;  // two 64-row blocks of dW per unit
-    const void* kfn;
+    q.k_blocks = (int)((plan.N + plan.skinny_cols - 1) / plan.skinny_cols);
+    const int nb = plan.M > 64 ? 2 : 1;  // 64-row blocks of dW per unit
+    const int cb = plan.skinny_cols / 64;
+    const int okind = plan.splits > 1 ? OUT_PARTIAL : (out == DPG_BF16 ? OUT_BF16 : OUT_F32);
+    const void* kfn = (const void*)lookup_skinny_kernel(nb, cb, okind);
+    if (!kfn) return DPG_ERR_INVALID_ARG;
     if (plan.splits > 1) {
       q.out = ws;
       q.ldo = plan.N;
       q.split_stride = plan.M * plan.N;
-      kfn = wide ? (const void*)&skinny_wgrad_kernel<2, OUT_PARTIAL> : (const void*)&skinny_wgrad_kernel<1, OUT_PARTIAL>;
     } else {
       q.out = c;
       q.ldo = ldc;
       q.split_stride = 0;
-      if (out == DPG_BF16)
-        kfn = wide ? (const void*)&skinny_wgrad_kernel<2, OUT_BF16> : (const void*)&skinny_wgrad_kernel<1, OUT_BF16>;
-      else
-        kfn = wide ? (const void*)&skinny_wgrad_kernel<2, OUT_F32> : (const void*)&skinny_wgrad_kernel<1, OUT_F32>;
     }
     void* sargs[] = {&q};
-    const unsigned sgrid = (unsigned)q.k_blocks * (unsigned)plan.splits;
-    hipError_t e = hipLaunchKernel(kfn, dim3(sgrid), dim3(512), sargs, 0, stream);
+    hipError_t e = hipLaunchKernel(kfn, dim3((unsigned)plan.grid), dim3(512), sargs, 0, stream);
     if (e != hipSuccess) return DPG_ERR_HIP;
     if (plan.splits > 1) return launch_reduce(plan, ws, c, ldc, out, stream);
     return DPG_OK;
@@ -299,7 +315,7 @@ dpg_status run(int pass, const void* a, int64_t lda, const void* b, int64_t ldb,
   const bool fast = plan.fast && ld_ok;
   const int threads = (fast && plan.tile == 0) ? 512 : tile_threads(plan.tile);
   // the pipelined kernel is persistent: one workgroup per CU slot walks its units
-  int64_t grid = plan.grid;
+  int64_t grid = plan.skinny ? (int64_t)plan.tiles_m * plan.tiles_n * plan.splits : plan.grid;
   if (fast) grid = std::min<int64_t>(grid, (int64_t)device_cus() * (plan.tile == 0 ? 1 : 2));
   hipError_t e = hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3(threads), args, 0, stream);
   if (e != hipSuccess) return DPG_ERR_HIP;

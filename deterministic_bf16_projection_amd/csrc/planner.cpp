@@ -86,9 +86,9 @@ bool make_plan(const PlanKey& key, Plan* p) {
   }
   p->kind = PLAN_GEMM;
   if (!p->x3 && p->layout == LAYOUT_WGRAD && p->M <= 128) {
-    // skinny weight gradient: units of (all N rows, 128 columns of K, token
-    // split); tiles_m / tiles_n keep the 64x64 tile counts of the generic
-    // kernel, which runs the plan when a leading dimension is too large
+    // skinny weight gradient: units of (all N rows, 128 or 64 columns of K,
+    // token split); tiles_m / tiles_n keep the 64x64 tile counts of the
+    // generic kernel, which runs the plan when a leading dimension is too large
     p->skinny = 1;
     p->tile = 2;
     p->tiles_m = (int)cdiv(p->M, 64);
@@ -105,8 +105,10 @@ bool make_plan(const PlanKey& key, Plan* p) {
     s = std::max<int64_t>(1, std::min<int64_t>(s, p->kt_total));
     p->kt_per_split = (int)cdiv(p->kt_total, s);
     p->splits = (int)cdiv(p->kt_total, p->kt_per_split);
+    // 64-column units when 128-column ones would leave more than half the CUs idle
+    p->skinny_cols = units * p->splits * 2 >= key.cus ? 128 : 64;
     p->group_m = 1;
-    p->grid = (int64_t)p->tiles_m * p->tiles_n * p->splits;  // generic-kernel grid
+    p->grid = cdiv(p->N, p->skinny_cols) * p->splits;
     p->ws_bytes = p->splits > 1 ? (size_t)p->splits * (size_t)p->M * (size_t)p->N * 4u : 0;
     const double bytes = 2.0 * (p->K * p->N + p->K * p->M) + (double)p->M * p->N * (p->splits > 1 ? 8.0 * p->splits : 4.0);
     p->est_us = bytes / kHbm * 1e6 + kLaunchUs * (p->splits > 1 ? 2 : 1);
@@ -159,7 +161,8 @@ int describe_plan(const PlanKey& key, const Plan& p, char* buf, size_t buflen) {
                   "pass=%s kind=gemm det=%d M=%lld N=%lld K=%lld layout=%s x3=%d out=%s tile=%dx%dx%d threads=%d "
                   "kernel=%s tiles=%dx%d group_m=%d splits=%d kt_total=%d kt_per_split=%d grid=%lld workspace=%zu est_us=%.1f",
                   kPass[key.pass], key.det, (long long)p.M, (long long)p.N, (long long)p.K, kLayout[p.layout], p.x3,
-                  p.out ? "f32" : "bf16", p.skinny ? 64 : ts.bm, p.skinny ? 64 : ts.bn, ts.bk,
+                  p.out ? "f32" : "bf16", p.skinny ? (int)cdiv(p.M, 64) * 64 : ts.bm, p.skinny ? p.skinny_cols : ts.bn,
+                  ts.bk,
                   (p.skinny || (p.fast && p.tile == 0)) ? 512 : ts.threads,
                   p.skinny ? "skinny" : (p.fast ? "pipelined" : "generic"), p.tiles_m, p.tiles_n, p.group_m, p.splits,
                   p.kt_total, p.kt_per_split, (long long)p.grid, p.ws_bytes, p.est_us);

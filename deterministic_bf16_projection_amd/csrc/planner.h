@@ -44,10 +44,11 @@ struct Plan {
   int tile;            // index into kTiles
   int fast;            // software-pipelined kernel (gemm_fast.h) instead of the generic one
   int skinny;          // streaming weight-gradient kernel for N <= 128 (skinny_wgrad.h)
+  int skinny_cols;     // columns of K per skinny work unit (64 or 128)
   int tiles_m, tiles_n;
   int splits, kt_total, kt_per_split;
   int group_m;
-  int64_t grid;        // workgroups of the GEMM launch
+  int64_t grid;        // workgroups of the GEMM launch (skinny: of the skinny kernel)
   size_t ws_bytes;     // FP32 partials: splits * M * N * 4 when splits > 1
   double est_us;       // model estimate
 };

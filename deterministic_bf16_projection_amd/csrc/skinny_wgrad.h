@@ -2,9 +2,10 @@
 //   dW[n, k] = sum_t dY[t, n] * X[t, k]
 // The pass reads X[T, K] once from HBM and is bandwidth-bound.
 //
-// Work unit = (all N rows, 128-column block of K, token split).  A workgroup
-// has 8 waves arranged as NB row blocks x 2 column blocks x TG token groups
-// (NB * 2 * TG = 8; NB = 1 for N <= 64, 2 for N <= 128), each wave owning a
+// Work unit = (all N rows, a block of CB * 64 columns of K, token split).  A
+// workgroup has 8 waves arranged as NB row blocks x CB column blocks x TG token
+// groups (NB * CB * TG = 8; NB = 1 for N <= 64, 2 for N <= 128; CB = 2, or 1
+// when a small forced split count leaves too few units), each wave owning a
 // 64 x 64 block of dW.  Per iteration, token group g takes the unit's 64-token
 // block (iteration * TG + g): its X tiles (64 tokens x 64 columns) and dY tiles
 // (64 tokens x 64 rows) are fetched once with 16-byte buffer loads (rows past T
@@ -27,15 +28,15 @@ struct SkinnyParams {
   int64_t lddy, ldx, ldo;
   int64_t split_stride;  // elements between workspace planes
   int T, N, K;
-  int k_blocks, splits;        // 128-column blocks of K; token splits
+  int k_blocks, splits;        // column blocks of K (CB * 64 columns); token splits
   int tb_total, tb_per_split;  // 64-token blocks and blocks per split
 };
 
-template <int NB, int OUT>
+template <int NB, int CB, int OUT>
 __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
   constexpr int W = 8;
-  constexpr int CB = 2;                 // 64-column blocks per unit
   constexpr int TG = W / (NB * CB);     // token groups
+  static_assert((NB == 1 || NB == 2) && (CB == 1 || CB == 2), "row and column blocks");
   constexpr int TILE = 4096;            // BF16 elements of one transposed 64x64 tile
   constexpr int X_TILES = CB * TG, Y_TILES = NB * TG;
   constexpr int RED_LD = 68;            // FP32 row stride of the reduction buffer
@@ -54,7 +55,7 @@ __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
   const int unit = xcd_remap(blockIdx.x, p.k_blocks * p.splits);
   const int split = unit / p.k_blocks;
   const int kb = unit - split * p.k_blocks;
-  const int c0 = kb * 128;
+  const int c0 = kb * (CB * 64);
   const int tb0 = split * p.tb_per_split;
   const int tb1 = min(tb0 + p.tb_per_split, p.tb_total);
   const int n_iter = (tb1 - tb0 + TG - 1) / TG;
@@ -178,7 +179,7 @@ __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
       }
   __syncthreads();
   // output block (nb, cb) = waves nb + NB * cb + NB * CB * g for g = 0..TG-1
-  constexpr int OUT_PER_THREAD = NB * CB * 64 * 64 / 512;  // elements per thread (16 or 32)
+  constexpr int OUT_PER_THREAD = NB * CB * 64 * 64 / 512;  // elements per thread (8, 16 or 32)
 #pragma unroll
   for (int h = 0; h < OUT_PER_THREAD / 8; ++h) {
     const int e = (tid + h * 512) * 8;           // element index in [NB*CB] x 64 x 64

@@ -211,6 +211,36 @@ def test_skinny_wgrad(skinny_x, T, K, N):
             assert torch.equal(again.view(torch.int16), out.view(torch.int16))
 
 
+# Exact-integer inputs through the skinny kernel: one and two 64-row blocks of
+# dW, 64- and 128-column units (auto plans use 128 columns when enough units
+# exist; forced small split counts use 64), ragged token tails.
+# (The planner's choices for these shapes are checked on the CPU.)
+SKINNY_EXACT = [
+    (4031, 128, 4096),   # two row blocks; 63 token blocks, last holds 63
+    (16384, 48, 5120),   # one row block, ragged N inside the block
+    (1025, 104, 1024),   # two row blocks, N ragged; 17 token blocks, last holds 1
+    (16384, 128, 4096),  # two row blocks, 128-column units
+]
+
+
+@pytest.mark.parametrize("T,N,K", SKINNY_EXACT)
+def test_skinny_exact_integer(T, N, K):
+    x, _, dy = dpg_inputs.dense(T, N, K, seed_group=9, kind="int")
+    ddy, dx_ = dev_bf16(dy), dev_bf16(x)
+    ii, jj = sample_positions(N, K, 3000, seed=T)
+    ref = oracle.wgrad(dy, x, rows=ii, cols=jj)
+    for det, split in [(True, 0), (False, 1), (False, 2), (True, 3)]:
+        for out_name in ("f32", "bf16"):
+            plan = dpg.parse_plan(dpg.plan_describe(dpg.PASS_WGRAD, T, N, K, OUT[out_name], det, split))
+            assert plan["kernel"] == "skinny", plan
+            out = _run("wgrad", ddy, dx_, OUT[out_name], det=det, split=split)
+            got = out[torch.from_numpy(ii).cuda(), torch.from_numpy(jj).cuda()]
+            if out_name == "f32":
+                np.testing.assert_array_equal(host_f64(got), ref)
+            else:
+                np.testing.assert_array_equal(host_bits(got), oracle.f64_to_bf16(ref))
+
+
 # ------------------------------------------- checkpointed step 2fwd + bwd --
 @pytest.mark.parametrize("N", [1024, 512])
 def test_checkpointed_step(N):

@@ -68,6 +68,27 @@ def test_forced_split_one():
     assert p["splits"] == "1" and p["workspace"] == "0"
 
 
+def test_skinny_unit_shapes():
+    """Skinny weight gradients: 128-column units when they give at least half
+    as many workgroups as CUs, 64-column units otherwise (forced small split
+    counts); one or two 64-row blocks of dW.  The exact-integer GPU shapes
+    together reach all four kernel variants."""
+    def tile(T, N, K, det, split):
+        p = plan(2, T, N, K, out=F32, det=det, split=split)
+        assert p["kernel"] == "skinny", p
+        return p["tile"]
+    assert tile(16384, 64, 4096, 1, 0) == "64x128x64"
+    assert tile(16384, 128, 4096, 1, 0) == "128x128x64"
+    assert tile(16384, 64, 4096, 0, 2) == "64x64x64"
+    assert tile(16384, 128, 4096, 0, 1) == "128x64x64"
+    assert tile(16384, 48, 5120, 1, 0) == "64x128x64"
+    seen = set()
+    for T, N, K in [(4031, 128, 4096), (16384, 48, 5120), (1025, 104, 1024), (16384, 128, 4096)]:
+        for det, split in [(1, 0), (0, 1), (0, 2), (1, 3)]:
+            seen.add(tile(T, N, K, det, split))
+    assert seen == {"64x64x64", "64x128x64", "128x64x64", "128x128x64"}
+
+
 def test_router_uses_bf16x3():
     p = plan(3, 64, 256, 4096, out=F32)
     assert p["x3"] == "1"
