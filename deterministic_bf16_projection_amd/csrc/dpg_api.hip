@@ -179,15 +179,16 @@ dpg_status check_mat(const Mat& m) {
 
 // fixed-order sum of the split partials in the workspace, converted to the output type
 dpg_status launch_reduce(const Plan& plan, void* ws, void* c, int64_t ldc, int out, hipStream_t stream) {
-  const int64_t quads = plan.M * (plan.N / 4);
-  const int grid = (int)std::min<int64_t>((quads + 255) / 256, 8192);
+  // x: 256 quads of a row per workgroup; y: rows, up to about 2048 workgroups in all
+  const int gx = (int)((plan.N / 4 + 255) / 256);
+  const int gy = (int)std::max<int64_t>(1, std::min<int64_t>(plan.M, std::max(1, 2048 / gx)));
   const float* wsf = (const float*)ws;
   int S = plan.splits, M = (int)plan.M, Nn = (int)plan.N;
   int64_t stride = plan.M * plan.N;
   void* rargs[] = {&wsf, &S, &stride, &M, &Nn, &c, &ldc};
   hipError_t e = hipLaunchKernel(out == DPG_BF16 ? (const void*)&splitk_reduce_kernel<OUT_BF16>
                                                  : (const void*)&splitk_reduce_kernel<OUT_F32>,
-                                 dim3(grid), dim3(256), rargs, 0, stream);
+                                 dim3(gx, gy), dim3(256), rargs, 0, stream);
   return e == hipSuccess ? DPG_OK : DPG_ERR_HIP;
 }
 

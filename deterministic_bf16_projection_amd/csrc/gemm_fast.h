@@ -436,7 +436,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_fast_kernel(Ge
   __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (BM + BN) * BK];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: SGPR
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   if constexpr (NT == 512) {
     if (wave < 4)

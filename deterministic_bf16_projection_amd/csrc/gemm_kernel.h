@@ -297,17 +297,32 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_kernel(GemmParams p) {
 
 // ------------------------------------------------------ split-K reduction --
 // out[m, n] = sum over s = 0, 1, ..., S-1 of ws[s][m][n], in that order, then
-// converted to the output type.  Four columns per thread (N % 8 == 0).
+// converted to the output type.  Four columns per thread (N % 8 == 0); grid x
+// covers the quads of a row, grid y strides over rows.  The loads of four
+// planes are issued together and then added one after another, so the sum
+// order stays ascending in s.
 template <int OUT>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ ws, int S, int64_t split_stride,
                                                             int M, int N, void* out, int64_t ldo) {
-  const int64_t quads = (int64_t)M * (N / 4);
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t m = q / (N / 4);
-    const int n = (int)(q % (N / 4)) * 4;
-    const float* src = ws + m * N + n;
+  const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (n >= N) return;
+  for (int m = blockIdx.y; m < M; m += gridDim.y) {
+    const float* src = ws + (int64_t)m * N + n;
     f32x4 v = *(const f32x4*)src;
-    for (int s = 1; s < S; ++s) {
+    int s = 1;
+    for (; s + 4 <= S; s += 4) {
+      f32x4 w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) w[u] = *(const f32x4*)(src + (int64_t)(s + u) * split_stride);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[0] += w[u][0];
+        v[1] += w[u][1];
+        v[2] += w[u][2];
+        v[3] += w[u][3];
+      }
+    }
+    for (; s < S; ++s) {
       const f32x4 w = *(const f32x4*)(src + (int64_t)s * split_stride);
       v[0] += w[0];
       v[1] += w[1];
@@ -316,9 +331,9 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     }
     if (OUT == OUT_BF16) {
       u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      *(u32x2*)((unsigned short*)out + m * ldo + n) = o;
+      *(u32x2*)((unsigned short*)out + (int64_t)m * ldo + n) = o;
     } else {
-      *(f32x4*)((float*)out + m * ldo + n) = v;
+      *(f32x4*)((float*)out + (int64_t)m * ldo + n) = v;
     }
   }
 }

@@ -46,7 +46,8 @@ __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
   __shared__ __attribute__((aligned(16))) float smem_f[SMEM_FLOATS];
   __bf16* smem = (__bf16*)smem_f;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index is uniform: keep it (and all that derives from it) in SGPRs
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   // wave -> (row block nb, column block cb, token group g)
   const int nb = wave % NB, cb = (wave / NB) % CB, g = wave / (NB * CB);
 
@@ -64,39 +65,60 @@ __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
   const __bf16* x = (const __bf16*)p.x;
   const int lddy = (int)p.lddy, ldx = (int)p.ldx;
 
-  // Staging: X tile (cb, g) is shared by the NB waves (*, cb, g) and dY tile
-  // (nb, g) by the CB waves (nb, *, g).  A tile is 8 x 8 sub-blocks of 8x8; lane
-  // (kc, sb) = (lane / 8, lane % 8) owns token rows kc*8.. and columns sb*8.., so
-  // the 8 lanes of one token row read 128 contiguous bytes; each of a tile's
-  // sharers fetches an equal range of token rows.
+  // Staging.  An iteration needs X_TILES + Y_TILES tiles of 64 tokens x 64
+  // columns; wave w fetches tile w + 8 r in round r (X tiles first, then dY
+  // tiles).  A tile is 8 x 8 sub-blocks of 8x8: lane (kc, sb) = (lane / 8,
+  // lane % 8) owns token rows kc*8.. and columns sb*8.., so the 8 lanes of one
+  // token row read 128 contiguous bytes.  With one round (N > 64 and 128-column
+  // units) the loads run two iterations ahead in two register buffers; with two
+  // rounds, one iteration ahead.
+  constexpr int TILES = X_TILES + Y_TILES;
+  constexpr int ROUNDS = (TILES + W - 1) / W;
+  constexpr int AHEAD = ROUNDS == 1 ? 2 : 1;
   const int kc = lane >> 3, sb = lane & 7;
-  const bool x_lane = kc / (8 / NB) == nb;
-  const bool y_lane = kc / (8 / CB) == cb;
   // Lanes with odd kc hold transposed column m ^ 1 in slot m (a per-lane choice
-  // of byte selectors), so that the 16 lanes of one LDS write phase cover rows of
-  // both parities; with the row swizzle the writes are then conflict-free.
+  // of byte selectors), so that the 16 lanes of one LDS write phase cover rows
+  // of both parities; with the row swizzle the writes are then conflict-free.
+  // Slot m goes to row sb*8 + (m ^ odd) of the tile, element offset lds0 ^ 72 m
+  // (the closed form of lds_chunk_off for these rows).
   const int odd = kc & 1;
   const uint32_t sel_even = odd ? 0x07060302u : 0x05040100u;
   const uint32_t sel_odd = odd ? 0x05040100u : 0x07060302u;
-  uint32_t voff_x[8], voff_y[8];
-  int lds_off[8];
-#pragma unroll
-  for (int l = 0; l < 8; ++l) {
-    voff_x[l] = (uint32_t)(((kc * 8 + l) * ldx + cb * 64 + sb * 8) * 2);
-    voff_y[l] = (uint32_t)(((kc * 8 + l) * lddy + nb * 64 + sb * 8) * 2);
-    const int row = sb * 8 + (l ^ odd);
-    lds_off[l] = lds_chunk_off(row, kc);
-  }
-  __bf16* x_tile = smem + (g * CB + cb) * TILE;            // shared with the NB waves (*, cb, g)
-  __bf16* y_tile = smem + (X_TILES + g * NB + nb) * TILE;  // shared with the CB waves (nb, *, g)
+  const int lds0 = (sb * 512) | (((9 * odd) ^ ((kc ^ sb) & 7)) << 3);
 
-  auto rsrc_rows = [&](const __bf16* base, int ld, int col0, int cols, int t0) {
-    const int rows = min(p.T - t0, 64);
-    int bytes = ((rows - 1) * ld + (cols - col0)) * 2;
-    bytes = rows > 0 ? max(bytes, 0) : 0;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(base + (int64_t)max(t0, 0) * ld + col0), (short)0,
-                                             bytes, 0x00020000);
+  // the tile this wave fetches in round r (wave-uniform)
+  struct Fetch {
+    const __bf16* base;  // first column of the tile's source rows
+    int ld, cols;        // row stride; readable columns from base
+    int g;               // token group
+    int valid;
+    __bf16* dst;         // LDS tile
   };
+  Fetch f[ROUNDS];
+  uint32_t voff[ROUNDS];
+#pragma unroll
+  for (int r = 0; r < ROUNDS; ++r) {
+    const int t = wave + W * r;
+    f[r].valid = t < TILES;
+    if (t < X_TILES) {  // X tile (g, cb'): columns c0 + cb' * 64 ..
+      const int cbt = t % CB;
+      f[r].g = t / CB;
+      f[r].base = x + c0 + cbt * 64;
+      f[r].ld = ldx;
+      f[r].cols = p.K - c0 - cbt * 64;
+    } else {  // dY tile (g, nb'): rows nb' * 64 .. of dW
+      const int yt = min(t, TILES - 1) - X_TILES;
+      const int nbt = yt % NB;
+      f[r].g = yt / NB;
+      f[r].base = dy + nbt * 64;
+      f[r].ld = lddy;
+      f[r].cols = p.N - nbt * 64;
+    }
+    f[r].dst = smem + min(t, TILES - 1) * TILE;
+    voff[r] = (uint32_t)((kc * 8 * f[r].ld + sb * 8) * 2);
+  }
+  __bf16* x_tile = smem + (g * CB + cb) * TILE;            // read by the NB waves (*, cb, g)
+  __bf16* y_tile = smem + (X_TILES + g * NB + nb) * TILE;  // read by the CB waves (nb, *, g)
 
   f32x16 acc[2][2];
 #pragma unroll
@@ -114,39 +136,43 @@ __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) koff[s] = ((2 * s + lh) ^ sw) << 3;
 
-  u32x4 gx[8], gy[8];
-  auto load = [&](int it) {
-    const int blk = tb0 + it * TG + g;
-    const int t0 = blk < tb1 ? blk * 64 : p.T;  // past this split: empty descriptors
-    if (x_lane) {
-      const rsrc_t rx = rsrc_rows(x, ldx, c0, p.K, t0);
+  // Buffer descriptor of round r's tile at iteration it: token rows
+  // [t0, min(T, t0 + 64)), columns [0, cols) from base; rows past T, columns
+  // past the matrix and iterations past the split read zeros (empty range).
+  auto rsrc = [&](int r, int it) {
+    const int blk = tb0 + it * TG + f[r].g;
+    const int t0 = blk < tb1 ? blk * 64 : p.T;
+    const int rows = min(p.T - t0, 64);
+    int bytes = ((rows - 1) * f[r].ld + f[r].cols) * 2;
+    bytes = (rows > 0 && f[r].cols > 0) ? max(bytes, 0) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(f[r].base + (int64_t)min(t0, p.T - 1) * f[r].ld),
+                                             (short)0, bytes, 0x00020000);
+  };
+  u32x4 gbuf[AHEAD][ROUNDS][8];
+  auto load = [&](u32x4(&gb)[ROUNDS][8], int it) {
 #pragma unroll
-      for (int l = 0; l < 8; ++l) gx[l] = buf_load16(rx, voff_x[l]);
-    }
-    if (y_lane) {
-      const rsrc_t ry = rsrc_rows(dy, lddy, 0, p.N, t0);
+    for (int r = 0; r < ROUNDS; ++r) {
+      if (f[r].valid) {
+        const rsrc_t rs = rsrc(r, it);
 #pragma unroll
-      for (int l = 0; l < 8; ++l) gy[l] = buf_load16(ry, voff_y[l]);
+        for (int l = 0; l < 8; ++l) gb[r][l] = buf_load16(rs, voff[r] + (uint32_t)(l * f[r].ld * 2));
+      }
     }
   };
-  auto stage = [&]() {
-    u32x4 t[8];
-    if (x_lane) {
-      transpose8x8_sel(gx, t, sel_even, sel_odd);
+  auto stage = [&](const u32x4(&gb)[ROUNDS][8]) {
+    int o = lds0;
+    asm volatile("" : "+v"(o));  // form the slot offsets here, not in the loop preheader
 #pragma unroll
-      for (int m = 0; m < 8; ++m) *(u32x4*)(x_tile + lds_off[m]) = t[m];
-    }
-    if (y_lane) {
-      transpose8x8_sel(gy, t, sel_even, sel_odd);
+    for (int r = 0; r < ROUNDS; ++r) {
+      if (f[r].valid) {
+        u32x4 t[8];
+        transpose8x8_sel(gb[r], t, sel_even, sel_odd);
 #pragma unroll
-      for (int m = 0; m < 8; ++m) *(u32x4*)(y_tile + lds_off[m]) = t[m];
+        for (int m = 0; m < 8; ++m) *(u32x4*)(f[r].dst + (o ^ (72 * m))) = t[m];
+      }
     }
   };
-
-  if (n_iter > 0) load(0);
-  for (int it = 0; it < n_iter; ++it) {
-    stage();
-    if (it + 1 < n_iter) load(it + 1);
+  auto compute = [&]() {
     __syncthreads();  // shared tiles complete
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -161,6 +187,20 @@ __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fb[j], fa[i], acc[i][j]);
     }
     __syncthreads();  // tiles consumed before the next iteration overwrites them
+  };
+
+  // iteration it is staged from buffer it % AHEAD; the buffer is refilled with
+  // iteration it + AHEAD right after staging (past the end: no memory access)
+#pragma unroll
+  for (int b = 0; b < AHEAD; ++b) load(gbuf[b], b);
+  for (int it = 0; it < n_iter; it += 2) {
+    stage(gbuf[0]);
+    load(gbuf[0], it + AHEAD);
+    compute();
+    if (it + 1 >= n_iter) break;
+    stage(gbuf[AHEAD - 1]);
+    load(gbuf[AHEAD - 1], it + 1 + AHEAD);
+    compute();
   }
 
   // ---- fixed-order reduction over the token groups: acc[i][j] holds D[k][n];
