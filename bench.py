@@ -293,7 +293,7 @@ def main():
             xs = to_dev(dpg_inputs.normal_bf16((T_SKINNY, K), 1.0, 0, 0))
             dys = to_dev(dpg_inputs.normal_bf16((T_SKINNY, N), 1.0, 0, 2))
             out = torch.empty((N, K), dtype=torch.float32, device=dev)
-            for det, split in [(True, 0), (False, 2)]:
+            for det, split in [(True, 0), (False, 1), (False, 2)]:
                 ws_n = dpg.workspace_size(dpg.PASS_WGRAD, T_SKINNY, N, K, torch.float32, det, split)
                 ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
                 for _ in range(5):
@@ -308,7 +308,8 @@ def main():
                 us = e0.elapsed_time(e1) * 1e3 / reps
                 nbytes = 2.0 * T_SKINNY * K + 2.0 * T_SKINNY * N + 4.0 * N * K
                 skinny.append({"shape": "%d->%d" % (K, N), "T": T_SKINNY, "out": "f32",
-                               "mode": "deterministic" if det else "split_k=2", "us": round(us, 2),
+                               "mode": "deterministic, planner splits" if det else "split_k=%d" % split,
+                               "us": round(us, 2),
                                "GBps": round(nbytes / us / 1e3, 1),
                                "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 4),
                                "plan": dpg.plan_describe(dpg.PASS_WGRAD, T_SKINNY, N, K, torch.float32, det, split)})
