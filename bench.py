@@ -13,6 +13,11 @@ at T = 16384, FP32 out) as GB/s of algorithmic HBM bytes against the 8 TB/s
 peak; the roofline of the dominant kernel from HIP events on the launch
 stream; and the FP64 oracle timed on the host cores on a bounded sample.
 
+Also timed (microseconds, eager and as a captured HIP graph): the 4096->1024
+projection at T = 64, the FP32 router at T = 64 / 256 / 1024 (deterministic
+and split-K), and the checkpointed FP32 step of 4096->1024 / 4096->512 at
+T = 16384.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 import argparse
@@ -198,6 +203,115 @@ def cpu_baseline(target_s=12.0):
                       % (rows, rows, dt)}
 
 
+def secondary_configs(dpg, dpg_inputs, torch, to_dev):
+    """The other measured workloads, microseconds per call: the 4096->1024
+    projection at T = 64 (BF16, deterministic), the FP32 router (E = 256,
+    H = 4096) at T = 64 / 256 / 1024 in deterministic and split-K (2) plans,
+    and the checkpointed step (forward, forward, input gradient, weight
+    gradient; FP32 out) of 4096->1024 and 4096->512 at T = 16384.  Each is
+    timed eagerly (host launch included) and as a captured HIP graph of the
+    same calls (device time only)."""
+    import numpy as np
+    dev = torch.device("cuda:0")
+
+    def timed(calls, reps=20):
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(3):
+                for c in calls:
+                    c()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            for c in calls:
+                c()
+        e1.record()
+        torch.cuda.synchronize()
+        eager = e0.elapsed_time(e1) * 1e3 / reps
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for _ in range(reps):
+                for c in calls:
+                    c()
+        g.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        graph = e0.elapsed_time(e1) * 1e3 / reps
+        return round(eager, 2), round(graph, 2)
+
+    def ws(pass_, T, N, K, out_dtype, det, split):
+        n = dpg.workspace_size(pass_, T, N, K, out_dtype, det, split)
+        return torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+
+    out = {}
+    # 4096 -> 1024 at T = 64
+    T, N, K = 64, 1024, 4096
+    x, w, dy = dpg_inputs.dense(T, N, K, seed_group=0)
+    X, W, DY = to_dev(x), to_dev(w), to_dev(dy)
+    Y = torch.empty((T, N), dtype=torch.bfloat16, device=dev)
+    DX = torch.empty((T, K), dtype=torch.bfloat16, device=dev)
+    DW = torch.empty((N, K), dtype=torch.bfloat16, device=dev)
+    wsf, wsd, wsw = (ws(p, T, N, K, torch.bfloat16, True, 0) for p in (0, 1, 2))
+    small = {}
+    for name, call in [("fwd", lambda: dpg.dpg_forward(X, W, out=Y, workspace=wsf)),
+                       ("dgrad", lambda: dpg.dpg_dgrad(DY, W, out=DX, workspace=wsd)),
+                       ("wgrad", lambda: dpg.dpg_wgrad(DY, X, out=DW, workspace=wsw))]:
+        e, g = timed([call])
+        small[name] = {"us_eager": e, "us_graph": g}
+    out["projection_4096x1024_T64_bf16"] = small
+
+    # router, FP32 via BF16x3
+    E, H = 256, 4096
+    router = {}
+    for T in (64, 256, 1024):
+        xr, wr, dyr = dpg_inputs.router(T, E, H, seed_group=0)
+        Xr, Wr, DYr = (torch.from_numpy(a).to(dev) for a in (xr, wr, dyr))
+        Yr = torch.empty((T, E), dtype=torch.float32, device=dev)
+        DXr = torch.empty((T, H), dtype=torch.float32, device=dev)
+        DWr = torch.empty((E, H), dtype=torch.float32, device=dev)
+        for det, split in [(True, 0), (False, 2)]:
+            w3 = [ws(p, T, E, H, torch.float32, det, split) for p in (3, 4, 5)]
+            fwd = lambda: dpg.dpg_router_forward(Xr, Wr, out=Yr, deterministic=det, split_k=split, workspace=w3[0])
+            dgr = lambda: dpg.dpg_router_dgrad(DYr, Wr, out=DXr, deterministic=det, split_k=split, workspace=w3[1])
+            wgr = lambda: dpg.dpg_router_wgrad(DYr, Xr, out=DWr, deterministic=det, split_k=split, workspace=w3[2])
+            rec = {}
+            for name, calls in [("fwd", [fwd]), ("dgrad", [dgr]), ("wgrad", [wgr]),
+                                ("2fwd+bwd", [fwd, fwd, dgr, wgr])]:
+                e, g = timed(calls)
+                rec[name] = {"us_eager": e, "us_graph": g}
+            router["T%d_%s" % (T, "det" if det else "split2")] = rec
+    out["router_E256_H4096_f32"] = router
+
+    # checkpointed step, FP32 out
+    T, K = 16384, 4096
+    xs = to_dev(dpg_inputs.normal_bf16((T, K), 1.0, 0, 0))
+    step = {}
+    for N in (1024, 512):
+        Ws = to_dev(dpg_inputs.normal_bf16((N, K), dpg_inputs.SIGMA_W, 0, 1))
+        DYs = to_dev(dpg_inputs.normal_bf16((T, N), 1.0, 0, 2))
+        Ys = torch.empty((T, N), dtype=torch.float32, device=dev)
+        DXs = torch.empty((T, K), dtype=torch.float32, device=dev)
+        DWs = torch.empty((N, K), dtype=torch.float32, device=dev)
+        w3 = [ws(p, T, N, K, torch.float32, True, 0) for p in (0, 1, 2)]
+        calls = [lambda: dpg.dpg_forward(xs, Ws, out=Ys, workspace=w3[0]),
+                 lambda: dpg.dpg_forward(xs, Ws, out=Ys, workspace=w3[0]),
+                 lambda: dpg.dpg_dgrad(DYs, Ws, out=DXs, workspace=w3[1]),
+                 lambda: dpg.dpg_wgrad(DYs, xs, out=DWs, workspace=w3[2])]
+        e, g = timed(calls, reps=10)
+        flop = 8.0 * T * N * K
+        step["4096x%d" % N] = {"us_eager": e, "us_graph": g, "tflops_graph": round(flop / g / 1e6, 1),
+                               "frac_peak_graph": round(flop / g / 1e6 / PEAK_BF16_TFLOPS, 4)}
+        del Ws, DYs, Ys, DXs, DWs
+    out["checkpointed_step_T16384_f32"] = step
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -205,6 +319,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-skinny", action="store_true")
+    ap.add_argument("--skip-secondary", action="store_true", help="skip the small, router and step timings")
     ap.add_argument("--profile-run", action="store_true", help="one step + a 1 GiB calibration copy (for rocprofv3)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "COMMAND"))
@@ -315,6 +430,8 @@ def main():
                                "plan": dpg.plan_describe(dpg.PASS_WGRAD, T_SKINNY, N, K, torch.float32, det, split)})
             del xs, dys, out
 
+    secondary = None if args.skip_secondary else secondary_configs(dpg, dpg_inputs, torch, to_dev)
+
     cpu = None if args.no_cpu_baseline else cpu_baseline()
 
     line = {
@@ -336,6 +453,7 @@ def main():
         "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "passes": per_pass,
         "skinny_wgrad": skinny,
+        "other_workloads": secondary,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernel_source_hash": kernel_source_hash(),
