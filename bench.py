@@ -15,7 +15,7 @@ stream; and the FP64 oracle timed on the host cores on a bounded sample.
 
 Also timed (microseconds, eager and as a captured HIP graph): the 4096->1024
 projection at T = 64, the FP32 router at T = 64 / 256 / 1024 (deterministic
-and split-K), and the checkpointed FP32 step of 4096->1024 / 4096->512 at
+split-K plans), and the checkpointed FP32 step of 4096->1024 / 4096->512 at
 T = 16384.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -206,7 +206,8 @@ def cpu_baseline(target_s=12.0):
 def secondary_configs(dpg, dpg_inputs, torch, to_dev):
     """The other measured workloads, microseconds per call: the 4096->1024
     projection at T = 64 (BF16, deterministic), the FP32 router (E = 256,
-    H = 4096) at T = 64 / 256 / 1024 in deterministic and split-K (2) plans,
+    H = 4096) at T = 64 / 256 / 1024 (deterministic split-K plans: the split
+    counts are reported),
     and the checkpointed step (forward, forward, input gradient, weight
     gradient; FP32 out) of 4096->1024 and 4096->512 at T = 16384.  Each is
     timed eagerly (host launch included) and as a captured HIP graph of the
@@ -275,7 +276,7 @@ def secondary_configs(dpg, dpg_inputs, torch, to_dev):
         Yr = torch.empty((T, E), dtype=torch.float32, device=dev)
         DXr = torch.empty((T, H), dtype=torch.float32, device=dev)
         DWr = torch.empty((E, H), dtype=torch.float32, device=dev)
-        for det, split in [(True, 0), (False, 2)]:
+        for det, split in [(True, 0)]:
             w3 = [ws(p, T, E, H, torch.float32, det, split) for p in (3, 4, 5)]
             fwd = lambda: dpg.dpg_router_forward(Xr, Wr, out=Yr, deterministic=det, split_k=split, workspace=w3[0])
             dgr = lambda: dpg.dpg_router_dgrad(DYr, Wr, out=DXr, deterministic=det, split_k=split, workspace=w3[1])
@@ -285,7 +286,9 @@ def secondary_configs(dpg, dpg_inputs, torch, to_dev):
                                 ("2fwd+bwd", [fwd, fwd, dgr, wgr])]:
                 e, g = timed(calls)
                 rec[name] = {"us_eager": e, "us_graph": g}
-            router["T%d_%s" % (T, "det" if det else "split2")] = rec
+            rec["splits"] = {n: int(dpg.parse_plan(dpg.plan_describe(p, T, E, H, torch.float32, det, split))["splits"])
+                             for n, p in (("fwd", 3), ("dgrad", 4), ("wgrad", 5))}
+            router["T%d" % T] = rec
     out["router_E256_H4096_f32"] = router
 
     # checkpointed step, FP32 out

@@ -45,9 +45,9 @@ KernelFn lookup_kernel(int tile, int layout, int x3, int out_kind) {
       {{DPG_ROW(TileL, 0, false), {nullptr, nullptr, nullptr}},
        {DPG_ROW(TileL, 1, false), {nullptr, nullptr, nullptr}},
        {DPG_ROW(TileL, 2, false), {nullptr, nullptr, nullptr}}},
-      {{DPG_ROW(TileM, 0, false), DPG_ROW(TileM, 0, true)},
-       {DPG_ROW(TileM, 1, false), DPG_ROW(TileM, 1, true)},
-       {DPG_ROW(TileM, 2, false), DPG_ROW(TileM, 2, true)}},
+      {{DPG_ROW(TileM, 0, false), {nullptr, nullptr, nullptr}},
+       {DPG_ROW(TileM, 1, false), {nullptr, nullptr, nullptr}},
+       {DPG_ROW(TileM, 2, false), {nullptr, nullptr, nullptr}}},
       {{DPG_ROW(TileS, 0, false), DPG_ROW(TileS, 0, true)},
        {DPG_ROW(TileS, 1, false), DPG_ROW(TileS, 1, true)},
        {DPG_ROW(TileS, 2, false), DPG_ROW(TileS, 2, true)}},

@@ -298,7 +298,7 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_kernel(GemmParams p) {
 // ------------------------------------------------------ split-K reduction --
 // out[m, n] = sum over s = 0, 1, ..., S-1 of ws[s][m][n], in that order, then
 // converted to the output type.  Four columns per thread (N % 8 == 0); grid x
-// covers the quads of a row, grid y strides over rows.  The loads of four
+// covers the quads of a row, grid y strides over rows.  The loads of eight
 // planes are issued together and then added one after another, so the sum
 // order stays ascending in s.
 template <int OUT>
@@ -310,12 +310,12 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     const float* src = ws + (int64_t)m * N + n;
     f32x4 v = *(const f32x4*)src;
     int s = 1;
-    for (; s + 4 <= S; s += 4) {
-      f32x4 w[4];
+    for (; s + 8 <= S; s += 8) {
+      f32x4 w[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) w[u] = *(const f32x4*)(src + (int64_t)(s + u) * split_stride);
+      for (int u = 0; u < 8; ++u) w[u] = *(const f32x4*)(src + (int64_t)(s + u) * split_stride);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         v[0] += w[u][0];
         v[1] += w[u][1];
         v[2] += w[u][2];

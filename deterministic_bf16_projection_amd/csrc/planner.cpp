@@ -8,18 +8,25 @@
 
 namespace dpg {
 
+// Rates are per CU, shared by the workgroups resident on it (measured on
+// MI355X: one 64x64 workgroup already sustains most of what a CU gives that
+// kernel).  BF16x3 plans use the 64x64 tile only (the larger generic tiles run
+// the three-product loop slower per CU).
 const TileShape kTiles[kNumTiles] = {
-    // bm, bn, bk, threads, occupancy, eff (sustained fraction of the CU MFMA rate), x3_ok, fast_ok
-    {256, 256, 64, 256, 1, 0.50, false, true},
-    {128, 128, 64, 256, 2, 0.36, true, true},
-    {64, 64, 64, 256, 4, 0.20, true, false},
+    // bm, bn, bk, threads, occupancy, eff, x3_eff, x3_ok, fast_ok
+    {256, 256, 64, 256, 1, 0.55, 0.0, false, true},
+    {128, 128, 64, 256, 2, 0.36, 0.0, false, true},
+    {64, 64, 64, 256, 4, 0.20, 0.19, true, false},
 };
 
 namespace {
 
 constexpr double kCuFlops = 2.2e15 / 256;  // sustained BF16 MFMA FLOP/s of one CU (measured loop)
 constexpr double kHbm = 5.0e12;            // sustained HBM bytes/s
-constexpr double kLaunchUs = 3.0;          // per extra kernel launch
+constexpr double kLaunchUs = 3.0;          // per kernel launch
+constexpr double kUnitUs = 1.0;            // fixed latency of a unit (first loads, last MFMAs)
+constexpr double kCuStore = 25e9;          // bytes/s of epilogue stores per CU
+constexpr double kReduceLatUs = 0.5;       // split reduction: per group of 8 dependent plane loads
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -39,11 +46,15 @@ void gemm_view(int pass, int64_t T, int64_t N, int64_t K, int64_t* m, int64_t* n
 }
 
 // Time model of one plan (microseconds).  The units (tile x split) run on
-// cus * occupancy workgroup slots in waves; a CU holding fewer workgroups than
-// its occupancy runs them at a proportionally lower rate.  Memory: operands
-// once, the output, and the split partials written and read back.
-double estimate_us(const TileShape& ts, int64_t M, int64_t N, int64_t K, int x3, int out_bytes, int in_bytes,
-                   int splits_req, int cus, int* splits_out, int* kt_per_out) {
+// cus * occupancy workgroup slots in rounds; the workgroups resident on a CU
+// share its rate.  A round costs the unit latency, the MFMA work and the
+// epilogue stores of its units; the persistent pipelined kernel pays latency
+// and one epilogue only once (later epilogues overlap the next unit's loads).
+// Memory: operands once and the output; split partials are written, then read
+// back by the reduce kernel, whose dependent loads cost latency when the
+// output is small.
+double estimate_us(const TileShape& ts, bool fast, int64_t M, int64_t N, int64_t K, int x3, int out_bytes,
+                   int in_bytes, int splits_req, int cus, int* splits_out, int* kt_per_out) {
   const int64_t tiles = cdiv(M, ts.bm) * cdiv(N, ts.bn);
   const int64_t kt_total = cdiv(K, ts.bk);
   int64_t s = std::min<int64_t>(splits_req, kt_total);
@@ -53,13 +64,16 @@ double estimate_us(const TileShape& ts, int64_t M, int64_t N, int64_t K, int x3,
   const double flop_unit = 2.0 * ts.bm * ts.bn * (double)(kt_per * ts.bk) * (x3 ? 3 : 1);
   const int64_t occ_used = std::min<int64_t>(ts.occupancy, cdiv(units, cus));
   const int64_t rounds = cdiv(units, (int64_t)cus * occ_used);
-  const double cu_rate = kCuFlops * ts.eff * (double)occ_used / ts.occupancy;  // whole CU
-  const double t_mfma = rounds * occ_used * flop_unit / cu_rate;
+  const double cu_rate = kCuFlops * (x3 ? ts.x3_eff : ts.eff);
+  const double epi_us = (double)occ_used * ts.bm * ts.bn * (s > 1 ? 4 : out_bytes) / kCuStore * 1e6;
+  const double mfma_round_us = (double)occ_used * flop_unit / cu_rate * 1e6;
+  double t_gemm = fast ? rounds * mfma_round_us + kUnitUs + epi_us : rounds * (mfma_round_us + kUnitUs + epi_us);
   const double bytes = (double)(M * K + N * K) * in_bytes + (double)M * N * out_bytes;
-  const double t_mem = bytes / kHbm;
-  double t = std::max(t_mfma, t_mem) * 1e6 + kLaunchUs;
-  // split partials: written by the GEMM, read back by the reduce kernel (not hidden)
-  if (s > 1) t += (double)M * N * 4.0 * (s + 1) / kHbm * 1e6 + kLaunchUs;
+  double t = std::max(t_gemm, bytes / kHbm * 1e6) + kLaunchUs;
+  if (s > 1) {
+    const double red_bytes = (double)M * N * 4.0 * (s + 1);
+    t += std::max(red_bytes / kHbm * 1e6, (double)cdiv(s, 8) * kReduceLatUs) + kLaunchUs;
+  }
   *splits_out = (int)s;
   *kt_per_out = (int)kt_per;
   return t;
@@ -124,7 +138,8 @@ bool make_plan(const PlanKey& key, Plan* p) {
     for (int sc : kSplitChoices) {
       if (key.split_req != 0 && sc != key.split_req) continue;
       int s, ktp;
-      const double t = estimate_us(ts, p->M, p->N, p->K, p->x3, out_bytes, in_bytes, sc, key.cus, &s, &ktp);
+      const bool fast = !p->x3 && ts.fast_ok && (p->layout == LAYOUT_WGRAD || p->K % 64 == 0);
+      const double t = estimate_us(ts, fast, p->M, p->N, p->K, p->x3, out_bytes, in_bytes, sc, key.cus, &s, &ktp);
       if (t < best * 0.97) {  // prefer the earlier (larger tile, fewer splits) choice unless 3% faster
         best = t;
         p->tile = ti;

@@ -15,8 +15,9 @@ struct TileShape {
   int bm, bn, bk;
   int threads;
   int occupancy;   // workgroups that fit one CU at once
-  double eff;      // sustained fraction of the CU's MFMA rate (model)
-  bool x3_ok;      // fits LDS with the BF16x3 hi and lo planes
+  double eff;      // sustained fraction of the CU's MFMA rate, BF16 operands (model)
+  double x3_eff;   // the same for BF16x3 (FP32 operands), counted in executed FLOP
+  bool x3_ok;      // BF16x3 plans use this tile
   bool fast_ok;    // a software-pipelined variant exists for this tile
 };
 constexpr int kNumTiles = 3;
