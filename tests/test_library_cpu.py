@@ -161,3 +161,25 @@ def test_validation_errors():
 def test_status_strings():
     for s in range(6):
         assert L.dpg_status_string(s)
+
+
+def test_deterministic_switch_resolution():
+    """torch.use_deterministic_algorithms(True) turns a fast-plan request into a
+    deterministic one, with a single warning."""
+    import warnings
+    import torch
+    from deterministic_bf16_projection_amd import autograd as dag
+    assert dag.resolve_deterministic(True) is True
+    prev = torch.are_deterministic_algorithms_enabled()
+    try:
+        torch.use_deterministic_algorithms(False)
+        assert dag.resolve_deterministic(False) is False
+        torch.use_deterministic_algorithms(True)
+        dag._warned[0] = False
+        with warnings.catch_warnings(record=True) as rec:
+            warnings.simplefilter("always")
+            assert dag.resolve_deterministic(False) is True
+            assert dag.resolve_deterministic(False) is True
+        assert len([r for r in rec if "deterministic" in str(r.message)]) == 1
+    finally:
+        torch.use_deterministic_algorithms(prev)
