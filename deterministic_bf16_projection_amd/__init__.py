@@ -7,7 +7,8 @@ output tensor.  All arithmetic runs in the library's gfx950 kernels.  There is
 no fallback: if ``libdpg.so`` is missing, importing this package raises.
 
 Names follow the C ABI: ``dpg_forward``, ``dpg_dgrad``, ``dpg_wgrad``,
-``dpg_router_forward``, ``dpg_router_dgrad``, ``dpg_router_wgrad``.
+``dpg_router_forward``, ``dpg_router_dgrad``, ``dpg_router_wgrad`` and the
+batched ``dpg_forward_batched``, ``dpg_dgrad_batched``, ``dpg_wgrad_batched``.
 ``deterministic=True`` is the default, as on the router page's description.
 """
 import ctypes
@@ -40,6 +41,18 @@ for _name in ("dpg_forward", "dpg_dgrad", "dpg_wgrad"):
 for _name in ("dpg_router_forward", "dpg_router_dgrad", "dpg_router_wgrad"):
     getattr(_lib, _name).argtypes = _ROUTER_ARGS
     getattr(_lib, _name).restype = _ci
+_BATCHED_ARGS = [_vp, _i64, _i64, _vp, _i64, _i64, _ci, _vp, _i64, _i64, _ci,
+                 _i64, _i64, _i64, _i64, _ci, _ci, _vp, _sz, _vp]
+for _name in ("dpg_forward_batched", "dpg_dgrad_batched"):
+    getattr(_lib, _name).argtypes = _BATCHED_ARGS
+    getattr(_lib, _name).restype = _ci
+_lib.dpg_wgrad_batched.argtypes = [_vp, _i64, _i64, _vp, _i64, _i64, _vp, _i64, _i64, _ci, _ci,
+                                   _i64, _i64, _i64, _i64, _ci, _ci, _vp, _sz, _vp]
+_lib.dpg_wgrad_batched.restype = _ci
+_lib.dpg_workspace_size_batched.argtypes = [_ci, _ci, _i64, _i64, _i64, _i64, _ci, _ci, _ci]
+_lib.dpg_workspace_size_batched.restype = _sz
+_lib.dpg_plan_describe_batched.argtypes = [_ci, _ci, _i64, _i64, _i64, _i64, _ci, _ci, _ci, ctypes.c_char_p, _sz]
+_lib.dpg_plan_describe_batched.restype = _ci
 _lib.dpg_workspace_size.argtypes = [_ci, _i64, _i64, _i64, _ci, _ci, _ci]
 _lib.dpg_workspace_size.restype = _sz
 _lib.dpg_plan_describe.argtypes = [_ci, _i64, _i64, _i64, _ci, _ci, _ci, ctypes.c_char_p, _sz]
@@ -248,3 +261,143 @@ def dpg_router_wgrad(dy, x, out=None, deterministic=True, split_k=0, workspace=N
         out = torch.empty((E, H), dtype=torch.float32, device=dy.device)
     return _call("dpg_router_wgrad", PASS_ROUTER_WGRAD, dy, x, out, F32, T, E, H, deterministic, split_k,
                  workspace, stream)
+
+
+# ------------------------------------------------------------------ batched --
+WEIGHT_LAYOUTS = {"nk": 0, "kn": 1}
+
+
+def _wl(weight_layout):
+    if weight_layout not in WEIGHT_LAYOUTS:
+        raise ValueError("weight_layout must be 'nk' or 'kn'")
+    return WEIGHT_LAYOUTS[weight_layout]
+
+
+def _batched(t, name, batch=None):
+    """(tensor, batch stride, row stride) of a [B, R, C] operand, or of a 2-D
+    [R, C] one shared by every problem (batch stride 0)."""
+    if t.dim() == 2:
+        t3, bstride = t, 0
+        rows, cols = t.shape
+        rs, cs = t.stride()
+    elif t.dim() == 3:
+        t3 = t
+        _, rows, cols = t.shape
+        bstride, rs, cs = t.stride()
+        if batch is not None and t.shape[0] != batch:
+            raise ValueError("%s: batch %d, expected %d" % (name, t.shape[0], batch))
+    else:
+        raise ValueError("%s must be [B, R, C] or [R, C]" % name)
+    if cols > 1 and cs != 1:
+        raise ValueError("%s: the last dimension must be contiguous" % name)
+    ld = rs if rows > 1 else ((cols + 7) // 8) * 8
+    return t3, bstride, ld
+
+
+def workspace_size_batched(pass_, batch, T, N, K, out_dtype=torch.bfloat16, deterministic=True, split_k=0,
+                           weight_layout="nk"):
+    return _lib.dpg_workspace_size_batched(pass_, _wl(weight_layout), batch, T, N, K, _code(out_dtype),
+                                           int(bool(deterministic)), split_k)
+
+
+def plan_describe_batched(pass_, batch, T, N, K, out_dtype=torch.bfloat16, deterministic=True, split_k=0,
+                          weight_layout="nk"):
+    buf = ctypes.create_string_buffer(1024)
+    st = _lib.dpg_plan_describe_batched(pass_, _wl(weight_layout), batch, T, N, K, _code(out_dtype),
+                                        int(bool(deterministic)), split_k, buf, 1024)
+    if st:
+        raise DpgError(st, "dpg_plan_describe_batched")
+    return buf.value.decode()
+
+
+def _batched_ws(pass_, wl, batch, T, N, K, out_code, det, split_k, workspace, device):
+    need = _lib.dpg_workspace_size_batched(pass_, wl, batch, T, N, K, out_code, det, split_k)
+    if need == ctypes.c_size_t(-1).value:
+        raise DpgError(1, "dpg_workspace_size_batched")
+    if need == 0:
+        return None, 0
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < need:
+        raise DpgError(4, "workspace")
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def dpg_forward_batched(x, w, out=None, out_dtype=torch.bfloat16, weight_layout="nk", deterministic=True,
+                        split_k=0, workspace=None, stream=None):
+    """y[b] = x[b] w[b]^T for weights [B, N, K] (weight_layout 'nk') or
+    y[b] = x[b] w[b] for weights [B, K, N] ('kn'); x [B, T, K]; a 2-D weight is
+    shared by every problem.  Views with any batch and row strides are taken as
+    they are (unit column stride)."""
+    _check_in(x, torch.bfloat16, "x")
+    _check_in(w, torch.bfloat16, "w")
+    wl = _wl(weight_layout)
+    batch, T, K = x.shape
+    N = w.shape[-2] if wl == 0 else w.shape[-1]
+    if (w.shape[-1] if wl == 0 else w.shape[-2]) != K:
+        raise ValueError("weight does not match K")
+    if out is None:
+        out = torch.empty((batch, T, N), dtype=out_dtype, device=x.device)
+    x3, sx, ldx = _batched(x, "x", batch)
+    w3, sw, ldw = _batched(w, "w", batch)
+    o3, so, ldo = _batched(out, "out", batch)
+    det = int(bool(deterministic))
+    ws, wsb = _batched_ws(PASS_FORWARD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace, x.device)
+    st = _lib.dpg_forward_batched(x3.data_ptr(), ldx, sx, w3.data_ptr(), ldw, sw, wl, o3.data_ptr(), ldo, so,
+                                  _code(out.dtype), batch, T, N, K, det, split_k,
+                                  ws.data_ptr() if ws is not None else None, wsb, _stream(stream))
+    if st:
+        raise DpgError(st, "dpg_forward_batched")
+    return out
+
+
+def dpg_dgrad_batched(dy, w, out=None, out_dtype=torch.bfloat16, weight_layout="nk", deterministic=True,
+                      split_k=0, workspace=None, stream=None):
+    """dx[b] = dy[b] w[b] for weights [B, N, K] ('nk'), or dy[b] w[b]^T for
+    weights [B, K, N] ('kn'); dy [B, T, N]."""
+    _check_in(dy, torch.bfloat16, "dy")
+    _check_in(w, torch.bfloat16, "w")
+    wl = _wl(weight_layout)
+    batch, T, N = dy.shape
+    K = w.shape[-1] if wl == 0 else w.shape[-2]
+    if (w.shape[-2] if wl == 0 else w.shape[-1]) != N:
+        raise ValueError("weight does not match N")
+    if out is None:
+        out = torch.empty((batch, T, K), dtype=out_dtype, device=dy.device)
+    d3, sd, ldd = _batched(dy, "dy", batch)
+    w3, sw, ldw = _batched(w, "w", batch)
+    o3, so, ldo = _batched(out, "out", batch)
+    det = int(bool(deterministic))
+    ws, wsb = _batched_ws(PASS_DGRAD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace, dy.device)
+    st = _lib.dpg_dgrad_batched(d3.data_ptr(), ldd, sd, w3.data_ptr(), ldw, sw, wl, o3.data_ptr(), ldo, so,
+                                _code(out.dtype), batch, T, N, K, det, split_k,
+                                ws.data_ptr() if ws is not None else None, wsb, _stream(stream))
+    if st:
+        raise DpgError(st, "dpg_dgrad_batched")
+    return out
+
+
+def dpg_wgrad_batched(dy, x, out=None, out_dtype=torch.bfloat16, weight_layout="nk", deterministic=True,
+                      split_k=0, workspace=None, stream=None):
+    """dw[b] = dy[b]^T x[b] as [B, N, K] ('nk') or x[b]^T dy[b] as [B, K, N]
+    ('kn'); dy [B, T, N], x [B, T, K]."""
+    _check_in(dy, torch.bfloat16, "dy")
+    _check_in(x, torch.bfloat16, "x")
+    wl = _wl(weight_layout)
+    batch, T, N = dy.shape
+    K = x.shape[-1]
+    if x.shape[-2] != T:
+        raise ValueError("x must be [B, T, K]")
+    if out is None:
+        out = torch.empty((batch, N, K) if wl == 0 else (batch, K, N), dtype=out_dtype, device=dy.device)
+    d3, sd, ldd = _batched(dy, "dy", batch)
+    x3, sx, ldx = _batched(x, "x", batch)
+    o3, so, ldo = _batched(out, "out", batch)
+    det = int(bool(deterministic))
+    ws, wsb = _batched_ws(PASS_WGRAD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace, dy.device)
+    st = _lib.dpg_wgrad_batched(d3.data_ptr(), ldd, sd, x3.data_ptr(), ldx, sx, o3.data_ptr(), ldo, so, wl,
+                                _code(out.dtype), batch, T, N, K, det, split_k,
+                                ws.data_ptr() if ws is not None else None, wsb, _stream(stream))
+    if st:
+        raise DpgError(st, "dpg_wgrad_batched")
+    return out

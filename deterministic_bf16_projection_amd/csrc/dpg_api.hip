@@ -111,6 +111,8 @@ struct KeyHash {
     mix((uint64_t)k.det);
     mix((uint64_t)k.split_req);
     mix((uint64_t)k.cus);
+    mix((uint64_t)k.batch);
+    mix((uint64_t)k.wlayout);
     return (size_t)h;
   }
 };
@@ -178,69 +180,112 @@ dpg_status check_mat(const Mat& m) {
 }
 
 // fixed-order sum of the split partials in the workspace, converted to the output type
-dpg_status launch_reduce(const Plan& plan, void* ws, void* c, int64_t ldc, int out, hipStream_t stream) {
-  // x: 256 quads of a row per workgroup; y: rows, up to about 2048 workgroups in all
+dpg_status launch_reduce(const Plan& plan, void* ws, void* c, int64_t ldc, int64_t c_batch, int out,
+                         hipStream_t stream) {
+  // x: 256 quads of a row per workgroup; y: rows of all problems, up to about
+  // 2048 workgroups in all
   const int gx = (int)((plan.N / 4 + 255) / 256);
-  const int gy = (int)std::max<int64_t>(1, std::min<int64_t>(plan.M, std::max(1, 2048 / gx)));
+  const int gy = (int)std::max<int64_t>(1, std::min<int64_t>(plan.M * plan.batch, std::max(1, 2048 / gx)));
   const float* wsf = (const float*)ws;
   int S = plan.splits, M = (int)plan.M, Nn = (int)plan.N;
   int64_t stride = plan.M * plan.N;
-  void* rargs[] = {&wsf, &S, &stride, &M, &Nn, &c, &ldc};
+  int64_t batch = plan.batch;
+  void* rargs[] = {&wsf, &S, &stride, &M, &Nn, &c, &ldc, &batch, &c_batch};
   hipError_t e = hipLaunchKernel(out == DPG_BF16 ? (const void*)&splitk_reduce_kernel<OUT_BF16>
                                                  : (const void*)&splitk_reduce_kernel<OUT_F32>,
                                  dim3(gx, gy), dim3(256), rargs, 0, stream);
   return e == hipSuccess ? DPG_OK : DPG_ERR_HIP;
 }
 
+// One operand or output of a call: pointer, row stride, shape, element size
+// and the stride between consecutive problems of a batched call.
+struct Operand {
+  const void* ptr;
+  int64_t ld, rows, cols;
+  int elt;
+  int64_t bstride;
+};
+
+dpg_status check_operand(const Operand& o, int64_t batch, bool output) {
+  dpg_status st = check_mat(Mat{o.ptr, o.ld, o.rows, o.cols, o.elt});
+  if (st != DPG_OK) return st;
+  if (o.cols % 8) return DPG_ERR_ALIGNMENT;
+  if (batch > 1 && o.rows > 0 && o.cols > 0) {
+    if (o.bstride < 0) return DPG_ERR_INVALID_ARG;
+    if ((o.bstride * o.elt) % 16 != 0) return DPG_ERR_ALIGNMENT;
+    // outputs of different problems must not overlap: either stacked (each
+    // problem past the previous one's last element) or interleaved within
+    // rows (disjoint column ranges of one row stride)
+    if (output) {
+      const bool stacked = o.bstride >= (o.rows - 1) * o.ld + o.cols;
+      const bool interleaved = o.bstride >= o.cols && (batch - 1) * o.bstride + o.cols <= o.ld;
+      if (!stacked && !interleaved) return DPG_ERR_INVALID_ARG;
+    }
+  }
+  return DPG_OK;
+}
+
 // ---------------------------------------------------------------- launch --
-dpg_status run(int pass, const void* a, int64_t lda, const void* b, int64_t ldb, void* c, int64_t ldc, int out,
-               int64_t T, int64_t N, int64_t K, int det, int split_k, void* ws, size_t ws_bytes,
-               hipStream_t stream) {
+// Runs `batch` problems of one pass.  For the projection passes (a, b) are
+// (x, w), (dy, w) and (dy, x) as in the entry points; `wlayout` says whether the
+// weight (for the weight gradient: the output) is stored [N,K] or [K,N].
+dpg_status run(int pass, int wlayout, int64_t batch, const void* a, int64_t lda, int64_t sa, const void* b,
+               int64_t ldb, int64_t sb, void* c, int64_t ldc, int64_t sc, int out, int64_t T, int64_t N, int64_t K,
+               int det, int split_k, void* ws, size_t ws_bytes, hipStream_t stream) {
   if (out != DPG_BF16 && out != DPG_F32) return DPG_ERR_INVALID_ARG;
-  if (T < 0 || N < 0 || K < 0) return DPG_ERR_INVALID_ARG;
+  if (T < 0 || N < 0 || K < 0 || batch < 0) return DPG_ERR_INVALID_ARG;
+  if (wlayout != WEIGHT_NK && wlayout != WEIGHT_KN) return DPG_ERR_INVALID_ARG;
   if (split_k < 0 || split_k > 64) return DPG_ERR_UNSUPPORTED;
   const int in_elt = pass >= 3 ? 4 : 2;
   const int out_elt = out == DPG_F32 ? 4 : 2;
-  // operand and output shapes as the caller sees them
-  Mat ma, mb, mc;
+  const bool kn = wlayout == WEIGHT_KN;
+  // operand and output shapes as the caller holds them
+  Operand ma, mb, mc;
   switch (pass % 3) {
-    case 0:  // Y[T,N] = X[T,K] W[N,K]^T
-      ma = {a, lda, T, K, in_elt};
-      mb = {b, ldb, N, K, in_elt};
-      mc = {c, ldc, T, N, out_elt};
+    case 0:  // Y[T,N] = X[T,K] W^T, W [N,K] or [K,N]
+      ma = {a, lda, T, K, in_elt, sa};
+      mb = kn ? Operand{b, ldb, K, N, in_elt, sb} : Operand{b, ldb, N, K, in_elt, sb};
+      mc = {c, ldc, T, N, out_elt, sc};
       break;
-    case 1:  // dX[T,K] = dY[T,N] W[N,K]
-      ma = {a, lda, T, N, in_elt};
-      mb = {b, ldb, N, K, in_elt};
-      mc = {c, ldc, T, K, out_elt};
+    case 1:  // dX[T,K] = dY[T,N] W
+      ma = {a, lda, T, N, in_elt, sa};
+      mb = kn ? Operand{b, ldb, K, N, in_elt, sb} : Operand{b, ldb, N, K, in_elt, sb};
+      mc = {c, ldc, T, K, out_elt, sc};
       break;
-    default:  // dW[N,K] = dY[T,N]^T X[T,K]
-      ma = {a, lda, T, N, in_elt};
-      mb = {b, ldb, T, K, in_elt};
-      mc = {c, ldc, N, K, out_elt};
+    default:  // dW = dY^T X into [N,K], or X^T dY into [K,N]
+      ma = {a, lda, T, N, in_elt, sa};
+      mb = {b, ldb, T, K, in_elt, sb};
+      mc = kn ? Operand{c, ldc, K, N, out_elt, sc} : Operand{c, ldc, N, K, out_elt, sc};
       break;
   }
   dpg_status st;
-  if ((st = check_mat(ma)) != DPG_OK) return st;
-  if ((st = check_mat(mb)) != DPG_OK) return st;
-  if ((st = check_mat(mc)) != DPG_OK) return st;
-  // a matrix whose other extent is nonzero needs its column count checked even when
-  // it is the reduction side of an empty product
-  if ((ma.cols % 8) || (mb.cols % 8) || (mc.cols % 8)) return DPG_ERR_ALIGNMENT;
+  if ((st = check_operand(ma, batch, false)) != DPG_OK) return st;
+  if ((st = check_operand(mb, batch, false)) != DPG_OK) return st;
+  if ((st = check_operand(mc, batch, true)) != DPG_OK) return st;
 
+  PlanKey key = make_key(pass, T, N, K, out, det, split_k, true);
+  key.batch = batch;
+  key.wlayout = wlayout;
   Plan plan;
-  if (!get_plan(make_key(pass, T, N, K, out, det, split_k, true), &plan)) return DPG_ERR_INVALID_ARG;
+  if (!get_plan(key, &plan)) return DPG_ERR_INVALID_ARG;
   if (plan.kind == PLAN_NOOP) return DPG_OK;
   if (plan.ws_bytes > 0) {
     if (ws_bytes < plan.ws_bytes) return DPG_ERR_WORKSPACE;
     if (!ws || !aligned16(ws)) return DPG_ERR_WORKSPACE;
   }
+  // GEMM operands: a weight gradient into [K,N] takes X as A and dY as B
+  if (plan.swap_ab) {
+    std::swap(a, b);
+    std::swap(lda, ldb);
+    std::swap(sa, sb);
+  }
 
   if (plan.kind == PLAN_ZERO) {
-    const int64_t quads = plan.M * (plan.N / 4);
+    const int64_t quads = batch * plan.M * (plan.N / 4);
     const int grid = (int)std::min<int64_t>((quads + 255) / 256, 4096);
     int M = (int)plan.M, Nn = (int)plan.N;
-    void* args[] = {&M, &Nn, &c, &ldc};
+    int64_t bt = batch;
+    void* args[] = {&M, &Nn, &c, &ldc, &bt, &sc};
     hipError_t e = hipLaunchKernel(out == DPG_BF16 ? (const void*)&zero_fill_kernel<OUT_BF16>
                                                    : (const void*)&zero_fill_kernel<OUT_F32>,
                                    dim3(grid), dim3(256), args, 0, stream);
@@ -277,7 +322,7 @@ dpg_status run(int pass, const void* a, int64_t lda, const void* b, int64_t ldb,
     void* sargs[] = {&q};
     hipError_t e = hipLaunchKernel(kfn, dim3((unsigned)plan.grid), dim3(512), sargs, 0, stream);
     if (e != hipSuccess) return DPG_ERR_HIP;
-    if (plan.splits > 1) return launch_reduce(plan, ws, c, ldc, out, stream);
+    if (plan.splits > 1) return launch_reduce(plan, ws, c, ldc, sc, out, stream);
     return DPG_OK;
   }
 
@@ -295,16 +340,21 @@ dpg_status run(int pass, const void* a, int64_t lda, const void* b, int64_t ldb,
   p.kt_total = plan.kt_total;
   p.kt_per_split = plan.kt_per_split;
   p.group_m = plan.group_m;
+  p.batch = (int)batch;
+  p.batch_a = sa;
+  p.batch_b = sb;
   int out_kind;
   if (plan.splits > 1) {
     p.c = ws;
     p.ldc = plan.N;
     p.split_stride = plan.M * plan.N;
+    p.batch_c = (int64_t)plan.splits * p.split_stride;
     out_kind = OUT_PARTIAL;
   } else {
     p.c = c;
     p.ldc = ldc;
     p.split_stride = 0;
+    p.batch_c = sc;
     out_kind = out == DPG_BF16 ? OUT_BF16 : OUT_F32;
   }
   // the pipelined kernel addresses each tile through 32-bit buffer offsets
@@ -320,8 +370,16 @@ dpg_status run(int pass, const void* a, int64_t lda, const void* b, int64_t ldb,
   if (fast) grid = std::min<int64_t>(grid, (int64_t)device_cus() * (plan.tile == 0 ? 1 : 2));
   hipError_t e = hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3(threads), args, 0, stream);
   if (e != hipSuccess) return DPG_ERR_HIP;
-  if (plan.splits > 1) return launch_reduce(plan, ws, c, ldc, out, stream);
+  if (plan.splits > 1) return launch_reduce(plan, ws, c, ldc, sc, out, stream);
   return DPG_OK;
+}
+
+// the single-problem form used by the unbatched entry points
+dpg_status run(int pass, const void* a, int64_t lda, const void* b, int64_t ldb, void* c, int64_t ldc, int out,
+               int64_t T, int64_t N, int64_t K, int det, int split_k, void* ws, size_t ws_bytes,
+               hipStream_t stream) {
+  return run(pass, WEIGHT_NK, 1, a, lda, 0, b, ldb, 0, c, ldc, 0, out, T, N, K, det, split_k, ws, ws_bytes,
+             stream);
 }
 
 }  // namespace
@@ -371,6 +429,55 @@ dpg_status dpg_router_wgrad(const float* dy, int64_t lddy, const float* x, int64
                             size_t workspace_bytes, hipStream_t stream) {
   return run(DPG_PASS_ROUTER_WGRAD, dy, lddy, x, ldx, dw, lddw, DPG_F32, T, E, H, deterministic, split_k, workspace,
              workspace_bytes, stream);
+}
+
+dpg_status dpg_forward_batched(const void* x, int64_t ldx, int64_t stride_x, const void* w, int64_t ldw,
+                               int64_t stride_w, dpg_weight_layout w_layout, void* y, int64_t ldy, int64_t stride_y,
+                               dpg_dtype y_dtype, int64_t batch, int64_t T, int64_t N, int64_t K, int deterministic,
+                               int split_k, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run(DPG_PASS_FORWARD, (int)w_layout, batch, x, ldx, stride_x, w, ldw, stride_w, y, ldy, stride_y, y_dtype,
+             T, N, K, deterministic, split_k, workspace, workspace_bytes, stream);
+}
+
+dpg_status dpg_dgrad_batched(const void* dy, int64_t lddy, int64_t stride_dy, const void* w, int64_t ldw,
+                             int64_t stride_w, dpg_weight_layout w_layout, void* dx, int64_t lddx, int64_t stride_dx,
+                             dpg_dtype dx_dtype, int64_t batch, int64_t T, int64_t N, int64_t K, int deterministic,
+                             int split_k, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run(DPG_PASS_DGRAD, (int)w_layout, batch, dy, lddy, stride_dy, w, ldw, stride_w, dx, lddx, stride_dx,
+             dx_dtype, T, N, K, deterministic, split_k, workspace, workspace_bytes, stream);
+}
+
+dpg_status dpg_wgrad_batched(const void* dy, int64_t lddy, int64_t stride_dy, const void* x, int64_t ldx,
+                             int64_t stride_x, void* dw, int64_t lddw, int64_t stride_dw, dpg_weight_layout w_layout,
+                             dpg_dtype dw_dtype, int64_t batch, int64_t T, int64_t N, int64_t K, int deterministic,
+                             int split_k, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run(DPG_PASS_WGRAD, (int)w_layout, batch, dy, lddy, stride_dy, x, ldx, stride_x, dw, lddw, stride_dw,
+             dw_dtype, T, N, K, deterministic, split_k, workspace, workspace_bytes, stream);
+}
+
+size_t dpg_workspace_size_batched(dpg_pass pass, dpg_weight_layout w_layout, int64_t batch, int64_t T, int64_t N,
+                                  int64_t K, dpg_dtype out_dtype, int deterministic, int split_k) {
+  if ((int)pass < 0 || (int)pass >= 3) return (size_t)-1;
+  PlanKey key = make_key((int)pass, T, N, K, (int)out_dtype, deterministic, split_k, true);
+  key.batch = batch;
+  key.wlayout = (int)w_layout;
+  Plan plan;
+  if (!get_plan(key, &plan)) return (size_t)-1;
+  return plan.kind == PLAN_GEMM ? plan.ws_bytes : 0;
+}
+
+dpg_status dpg_plan_describe_batched(dpg_pass pass, dpg_weight_layout w_layout, int64_t batch, int64_t T, int64_t N,
+                                     int64_t K, dpg_dtype out_dtype, int deterministic, int split_k, char* buf,
+                                     size_t buflen) {
+  if (!buf || buflen == 0) return DPG_ERR_INVALID_ARG;
+  if ((int)pass < 0 || (int)pass >= 3) return DPG_ERR_INVALID_ARG;
+  PlanKey key = make_key((int)pass, T, N, K, (int)out_dtype, deterministic, split_k, false);
+  key.batch = batch;
+  key.wlayout = (int)w_layout;
+  Plan plan;
+  if (!make_plan(key, &plan)) return DPG_ERR_INVALID_ARG;
+  describe_plan(key, plan, buf, buflen);
+  return DPG_OK;
 }
 
 size_t dpg_workspace_size(dpg_pass pass, int64_t T, int64_t N, int64_t K, dpg_dtype out_dtype, int deterministic,

@@ -194,6 +194,7 @@ __device__ __forceinline__ void sched_step() {
 // (shared A rows and B columns stay in that XCD's L2).
 struct UnitMap {
   int tiles_m, tiles_n, group_m, splits, kt_per, kt_total, total;
+  int per_batch;  // units of one problem (tiles x splits); total = per_batch x problems
 };
 
 // Position of a stream of (unit, K tile) steps.
@@ -203,6 +204,7 @@ struct StepCursor {
   int nkt, kt0;     // the unit's K tiles and first K tile
   int row0, col0;   // the unit's tile origin
   int split;
+  int b;            // the unit's problem
 };
 
 template <int BM, int BN>
@@ -211,7 +213,9 @@ __device__ __forceinline__ StepCursor cursor_at(const UnitMap& m, int unit) {
   c.u = unit;
   c.kt = 0;
   const int tiles = m.tiles_m * m.tiles_n;
-  const int pid = xcd_remap(min(unit, m.total - 1), m.total);
+  const int pid_all = xcd_remap(min(unit, m.total - 1), m.total);
+  c.b = pid_all / m.per_batch;
+  const int pid = pid_all - c.b * m.per_batch;
   const int split = pid / tiles;
   const int t = pid - split * tiles;
   const int per_group = m.group_m * m.tiles_n;
@@ -264,10 +268,10 @@ struct FastGemm {
     char* out;
     int64_t ldc;
     if (OUT == OUT_PARTIAL) {
-      out = (char*)p.c + (int64_t)c.split * p.split_stride * 4;
+      out = (char*)p.c + ((int64_t)c.b * p.batch_c + (int64_t)c.split * p.split_stride) * 4;
       ldc = p.ldc;
     } else {
-      out = (char*)p.c;
+      out = (char*)p.c + (int64_t)c.b * p.batch_c * (OUT == OUT_BF16 ? 2 : 4);
       ldc = p.ldc;
     }
 #pragma unroll
@@ -296,7 +300,7 @@ struct FastGemm {
     const __bf16* B = (const __bf16*)p.b;
     const int lda = (int)p.lda, ldb = (int)p.ldb;
     const UnitMap um = {p.tiles_m, p.tiles_n, p.group_m, p.splits, p.kt_per_split, p.kt_total,
-                        p.tiles_m * p.tiles_n * p.splits};
+                        p.tiles_m * p.tiles_n * p.splits * p.batch, p.tiles_m * p.tiles_n * p.splits};
     const int stride = gridDim.x;
     OpA opa;
     OpB opb;
@@ -346,8 +350,8 @@ struct FastGemm {
       // a step past the last unit gets empty descriptors (one row, no K left)
       const bool ok = cursor_valid(um, L);
       const int kk = ok ? (L.kt0 + L.kt) * BK : p.K;
-      if (DO_A) opa.load(tile_rsrc<A_KMAJ>(A, lda, L.row0, ok ? p.M : L.row0 + 1, kk, p.K));
-      if (DO_B) opb.load(tile_rsrc<B_KMAJ>(B, ldb, L.col0, ok ? p.N : L.col0 + 1, kk, p.K));
+      if (DO_A) opa.load(tile_rsrc<A_KMAJ>(A + L.b * p.batch_a, lda, L.row0, ok ? p.M : L.row0 + 1, kk, p.K));
+      if (DO_B) opb.load(tile_rsrc<B_KMAJ>(B + L.b * p.batch_b, ldb, L.col0, ok ? p.N : L.col0 + 1, kk, p.K));
     };
     auto store = [&](__bf16* stage) {
       if (DO_A) opa.store(stage);

@@ -35,6 +35,9 @@ struct GemmParams {
   int kt_total;      // ceil(K / BK)
   int kt_per_split;  // K tiles per split (the last split may hold fewer)
   int group_m;       // raster: tiles of one group run down this many tile rows
+  int batch;         // independent problems in the launch (units run over all of them)
+  int64_t batch_a, batch_b;  // elements between consecutive problems' A and B
+  int64_t batch_c;           // elements between outputs (workspace: splits * split_stride)
 };
 
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>
@@ -187,9 +190,12 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_kernel(GemmParams p) {
   const int wave = tid >> 6;
   const int wm = wave / Cfg::WAVES_N, wn = wave % Cfg::WAVES_N;
 
-  // tile and split of this workgroup
+  // problem, tile and split of this workgroup
   const int tiles = p.tiles_m * p.tiles_n;
-  const int pid = xcd_remap(blockIdx.x, tiles * p.splits);
+  const int per_batch = tiles * p.splits;
+  const int pid_all = xcd_remap(blockIdx.x, per_batch * p.batch);
+  const int bidx = pid_all / per_batch;
+  const int pid = pid_all - bidx * per_batch;
   const int split = pid / tiles;
   const int t = pid % tiles;
   const int per_group = p.group_m * p.tiles_n;
@@ -204,8 +210,9 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_kernel(GemmParams p) {
   const int kt1 = min(kt0 + p.kt_per_split, p.kt_total);
   const int nkt = kt1 - kt0;
 
-  const InT* A = (const InT*)p.a;
-  const InT* B = (const InT*)p.b;
+  const InT* A = (const InT*)p.a + bidx * p.batch_a;
+  const InT* B = (const InT*)p.b + bidx * p.batch_b;
+  const int64_t c_off = bidx * p.batch_c;
 
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -284,11 +291,11 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_kernel(GemmParams p) {
         if (row >= p.M) continue;
         const float v = acc[i][j][r];
         if (OUT == OUT_BF16) {
-          ((unsigned short*)p.c)[(int64_t)row * p.ldc + col] = (unsigned short)bf16_bits(v);
+          ((unsigned short*)p.c)[c_off + (int64_t)row * p.ldc + col] = (unsigned short)bf16_bits(v);
         } else if (OUT == OUT_F32) {
-          ((float*)p.c)[(int64_t)row * p.ldc + col] = v;
+          ((float*)p.c)[c_off + (int64_t)row * p.ldc + col] = v;
         } else {
-          ((float*)p.c)[(int64_t)split * p.split_stride + (int64_t)row * p.ldc + col] = v;
+          ((float*)p.c)[c_off + (int64_t)split * p.split_stride + (int64_t)row * p.ldc + col] = v;
         }
       }
     }
@@ -296,18 +303,22 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_kernel(GemmParams p) {
 }
 
 // ------------------------------------------------------ split-K reduction --
-// out[m, n] = sum over s = 0, 1, ..., S-1 of ws[s][m][n], in that order, then
-// converted to the output type.  Four columns per thread (N % 8 == 0); grid x
-// covers the quads of a row, grid y strides over rows.  The loads of eight
+// out[b][m, n] = sum over s = 0, 1, ..., S-1 of ws[b][s][m][n], in that order,
+// then converted to the output type.  Four columns per thread (N % 8 == 0);
+// grid x covers the quads of a row, grid y strides over the rows of all
+// problems.  The loads of eight
 // planes are issued together and then added one after another, so the sum
 // order stays ascending in s.
 template <int OUT>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ ws, int S, int64_t split_stride,
-                                                            int M, int N, void* out, int64_t ldo) {
+                                                            int M, int N, void* out, int64_t ldo, int64_t batch,
+                                                            int64_t out_batch) {
   const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (n >= N) return;
-  for (int m = blockIdx.y; m < M; m += gridDim.y) {
-    const float* src = ws + (int64_t)m * N + n;
+  for (int64_t mm = blockIdx.y; mm < batch * M; mm += gridDim.y) {
+    const int64_t b = mm / M;
+    const int m = (int)(mm - b * M);
+    const float* src = ws + b * S * split_stride + (int64_t)m * N + n;
     f32x4 v = *(const f32x4*)src;
     int s = 1;
     for (; s + 8 <= S; s += 8) {
@@ -331,24 +342,29 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     }
     if (OUT == OUT_BF16) {
       u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-      *(u32x2*)((unsigned short*)out + (int64_t)m * ldo + n) = o;
+      *(u32x2*)((unsigned short*)out + b * out_batch + (int64_t)m * ldo + n) = o;
     } else {
-      *(f32x4*)((float*)out + (int64_t)m * ldo + n) = v;
+      *(f32x4*)((float*)out + b * out_batch + (int64_t)m * ldo + n) = v;
     }
   }
 }
 
-// Zeros for an empty reduction: out[m, n] = 0 for m < M, n < N (N % 8 == 0).
+// Zeros for an empty reduction: out[b][m, n] = 0 for b < batch, m < M, n < N
+// (N % 8 == 0); problem b's output starts out_batch elements after b - 1's.
 template <int OUT>
-__global__ void __launch_bounds__(256) zero_fill_kernel(int M, int N, void* out, int64_t ldo) {
-  const int64_t quads = (int64_t)M * (N / 4);
+__global__ void __launch_bounds__(256) zero_fill_kernel(int M, int N, void* out, int64_t ldo, int64_t batch,
+                                                        int64_t out_batch) {
+  const int64_t quads = batch * M * (N / 4);
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < quads; q += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t m = q / (N / 4);
+    const int64_t mm = q / (N / 4);
+    const int64_t b = mm / M;
+    const int64_t m = mm - b * M;
     const int n = (int)(q % (N / 4)) * 4;
+    const int64_t off = b * out_batch + m * ldo + n;
     if (OUT == OUT_BF16) {
-      *(u32x2*)((unsigned short*)out + m * ldo + n) = u32x2{0u, 0u};
+      *(u32x2*)((unsigned short*)out + off) = u32x2{0u, 0u};
     } else {
-      *(f32x4*)((float*)out + m * ldo + n) = f32x4{0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)((float*)out + off) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   }
 }

@@ -30,17 +30,26 @@ constexpr double kReduceLatUs = 0.5;       // split reduction: per group of 8 de
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// GEMM view of a pass: C[M,N] = sum_k A(m,k) B(n,k).
-void gemm_view(int pass, int64_t T, int64_t N, int64_t K, int64_t* m, int64_t* n, int64_t* k, int* layout) {
+// GEMM view of a pass: C[M,N] = sum_k A(m,k) B(n,k).  A weight stored [K,N]
+// turns the forward's B and the input gradient's B around (MN-major <->
+// K-major); a weight gradient written [K,N] swaps the operands.
+void gemm_view(int pass, int wlayout, int64_t T, int64_t N, int64_t K, int64_t* m, int64_t* n, int64_t* k,
+               int* layout, int* swap_ab) {
+  *swap_ab = 0;
   switch (pass % 3) {
-    case 0:  // forward: Y[T,N] = X[T,K] W[N,K]^T
-      *m = T; *n = N; *k = K; *layout = LAYOUT_FWD;
+    case 0:  // forward: Y[T,N] = X[T,K] W^T
+      *m = T; *n = N; *k = K; *layout = wlayout == WEIGHT_KN ? LAYOUT_DGRAD : LAYOUT_FWD;
       break;
-    case 1:  // input gradient: dX[T,K] = dY[T,N] W[N,K]
-      *m = T; *n = K; *k = N; *layout = LAYOUT_DGRAD;
+    case 1:  // input gradient: dX[T,K] = dY[T,N] W
+      *m = T; *n = K; *k = N; *layout = wlayout == WEIGHT_KN ? LAYOUT_FWD : LAYOUT_DGRAD;
       break;
-    default:  // weight gradient: dW[N,K] = dY[T,N]^T X[T,K]
-      *m = N; *n = K; *k = T; *layout = LAYOUT_WGRAD;
+    default:  // weight gradient: dW = dY^T X (as [N,K]) or X^T dY (as [K,N])
+      if (wlayout == WEIGHT_KN) {
+        *m = K; *n = N; *swap_ab = 1;
+      } else {
+        *m = N; *n = K;
+      }
+      *k = T; *layout = LAYOUT_WGRAD;
       break;
   }
 }
@@ -53,9 +62,9 @@ void gemm_view(int pass, int64_t T, int64_t N, int64_t K, int64_t* m, int64_t* n
 // Memory: operands once and the output; split partials are written, then read
 // back by the reduce kernel, whose dependent loads cost latency when the
 // output is small.
-double estimate_us(const TileShape& ts, bool fast, int64_t M, int64_t N, int64_t K, int x3, int out_bytes,
-                   int in_bytes, int splits_req, int cus, int* splits_out, int* kt_per_out) {
-  const int64_t tiles = cdiv(M, ts.bm) * cdiv(N, ts.bn);
+double estimate_us(const TileShape& ts, bool fast, int64_t batch, int64_t M, int64_t N, int64_t K, int x3,
+                   int out_bytes, int in_bytes, int splits_req, int cus, int* splits_out, int* kt_per_out) {
+  const int64_t tiles = cdiv(M, ts.bm) * cdiv(N, ts.bn) * batch;
   const int64_t kt_total = cdiv(K, ts.bk);
   int64_t s = std::min<int64_t>(splits_req, kt_total);
   const int64_t kt_per = cdiv(kt_total, s);
@@ -68,10 +77,10 @@ double estimate_us(const TileShape& ts, bool fast, int64_t M, int64_t N, int64_t
   const double epi_us = (double)occ_used * ts.bm * ts.bn * (s > 1 ? 4 : out_bytes) / kCuStore * 1e6;
   const double mfma_round_us = (double)occ_used * flop_unit / cu_rate * 1e6;
   double t_gemm = fast ? rounds * mfma_round_us + kUnitUs + epi_us : rounds * (mfma_round_us + kUnitUs + epi_us);
-  const double bytes = (double)(M * K + N * K) * in_bytes + (double)M * N * out_bytes;
+  const double bytes = ((double)(M * K + N * K) * in_bytes + (double)M * N * out_bytes) * batch;
   double t = std::max(t_gemm, bytes / kHbm * 1e6) + kLaunchUs;
   if (s > 1) {
-    const double red_bytes = (double)M * N * 4.0 * (s + 1);
+    const double red_bytes = (double)M * N * 4.0 * (s + 1) * batch;
     t += std::max(red_bytes / kHbm * 1e6, (double)cdiv(s, 8) * kReduceLatUs) + kLaunchUs;
   }
   *splits_out = (int)s;
@@ -85,12 +94,16 @@ bool make_plan(const PlanKey& key, Plan* p) {
   if (key.pass < 0 || key.pass > 5 || key.T < 0 || key.N < 0 || key.K < 0) return false;
   if (key.out != 0 && key.out != 1) return false;
   if (key.split_req < 0 || key.split_req > 64) return false;
+  if (key.batch < 0 || key.batch > INT32_MAX / 2) return false;
+  if (key.wlayout != WEIGHT_NK && key.wlayout != WEIGHT_KN) return false;
+  if (key.pass >= 3 && (key.wlayout != WEIGHT_NK || key.batch != 1)) return false;  // router: single, [E,H]
   *p = Plan();
   p->x3 = key.pass >= 3;
   p->out = key.out;
-  gemm_view(key.pass, key.T, key.N, key.K, &p->M, &p->N, &p->K, &p->layout);
+  p->batch = key.batch;
+  gemm_view(key.pass, key.wlayout, key.T, key.N, key.K, &p->M, &p->N, &p->K, &p->layout, &p->swap_ab);
   if (p->M > INT32_MAX / 2 || p->N > INT32_MAX / 2 || p->K > INT32_MAX / 2) return false;
-  if (p->M == 0 || p->N == 0) {
+  if (p->M == 0 || p->N == 0 || p->batch == 0) {
     p->kind = PLAN_NOOP;
     return true;
   }
@@ -99,7 +112,7 @@ bool make_plan(const PlanKey& key, Plan* p) {
     return true;
   }
   p->kind = PLAN_GEMM;
-  if (!p->x3 && p->layout == LAYOUT_WGRAD && p->M <= 128) {
+  if (!p->x3 && p->layout == LAYOUT_WGRAD && p->M <= 128 && p->batch == 1 && !p->swap_ab) {
     // skinny weight gradient: units of (all N rows, 128 or 64 columns of K,
     // token split); tiles_m / tiles_n keep the 64x64 tile counts of the
     // generic kernel, which runs the plan when a leading dimension is too large
@@ -139,7 +152,8 @@ bool make_plan(const PlanKey& key, Plan* p) {
       if (key.split_req != 0 && sc != key.split_req) continue;
       int s, ktp;
       const bool fast = !p->x3 && ts.fast_ok && (p->layout == LAYOUT_WGRAD || p->K % 64 == 0);
-      const double t = estimate_us(ts, fast, p->M, p->N, p->K, p->x3, out_bytes, in_bytes, sc, key.cus, &s, &ktp);
+      const double t =
+          estimate_us(ts, fast, p->batch, p->M, p->N, p->K, p->x3, out_bytes, in_bytes, sc, key.cus, &s, &ktp);
       if (t < best * 0.97) {  // prefer the earlier (larger tile, fewer splits) choice unless 3% faster
         best = t;
         p->tile = ti;
@@ -157,8 +171,8 @@ bool make_plan(const PlanKey& key, Plan* p) {
   // the pipelined kernel needs whole 64-wide K tiles on K-major operands
   const bool kmajor_ok = p->layout == LAYOUT_WGRAD || (p->K % 64) == 0;
   p->fast = (!p->x3 && ts.fast_ok && kmajor_ok) ? 1 : 0;
-  p->grid = (int64_t)p->tiles_m * p->tiles_n * p->splits;
-  p->ws_bytes = p->splits > 1 ? (size_t)p->splits * (size_t)p->M * (size_t)p->N * 4u : 0;
+  p->grid = (int64_t)p->tiles_m * p->tiles_n * p->splits * p->batch;
+  p->ws_bytes = p->splits > 1 ? (size_t)p->batch * p->splits * (size_t)p->M * (size_t)p->N * 4u : 0;
   p->est_us = best;
   return p->grid <= INT32_MAX;
 }
@@ -174,13 +188,15 @@ int describe_plan(const PlanKey& key, const Plan& p, char* buf, size_t buflen) {
   const TileShape& ts = kTiles[p.tile];
   return snprintf(buf, buflen,
                   "pass=%s kind=gemm det=%d M=%lld N=%lld K=%lld layout=%s x3=%d out=%s tile=%dx%dx%d threads=%d "
-                  "kernel=%s tiles=%dx%d group_m=%d splits=%d kt_total=%d kt_per_split=%d grid=%lld workspace=%zu est_us=%.1f",
+                  "kernel=%s tiles=%dx%d group_m=%d splits=%d kt_total=%d kt_per_split=%d grid=%lld workspace=%zu est_us=%.1f "
+                  "batch=%lld weight=%s",
                   kPass[key.pass], key.det, (long long)p.M, (long long)p.N, (long long)p.K, kLayout[p.layout], p.x3,
                   p.out ? "f32" : "bf16", p.skinny ? (int)cdiv(p.M, 64) * 64 : ts.bm, p.skinny ? p.skinny_cols : ts.bn,
                   ts.bk,
                   (p.skinny || (p.fast && p.tile == 0)) ? 512 : ts.threads,
                   p.skinny ? "skinny" : (p.fast ? "pipelined" : "generic"), p.tiles_m, p.tiles_n, p.group_m, p.splits,
-                  p.kt_total, p.kt_per_split, (long long)p.grid, p.ws_bytes, p.est_us);
+                  p.kt_total, p.kt_per_split, (long long)p.grid, p.ws_bytes, p.est_us, (long long)p.batch,
+                  key.wlayout == WEIGHT_KN ? "kn" : "nk");
 }
 
 }  // namespace dpg

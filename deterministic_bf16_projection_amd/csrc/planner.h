@@ -23,6 +23,8 @@ struct TileShape {
 constexpr int kNumTiles = 3;
 extern const TileShape kTiles[kNumTiles];
 
+enum WeightLayout { WEIGHT_NK = 0, WEIGHT_KN = 1 };
+
 struct PlanKey {
   int pass;        // dpg_pass
   int64_t T, N, K;
@@ -30,9 +32,11 @@ struct PlanKey {
   int det;         // 0/1
   int split_req;   // 0 = auto
   int cus;         // CU count the plan was made for (fixed 256 in deterministic mode)
+  int64_t batch = 1;         // independent problems of the same shape in one launch
+  int wlayout = WEIGHT_NK;   // weight (or weight-gradient) stored [N,K] or [K,N]
   bool operator==(const PlanKey& o) const {
     return pass == o.pass && T == o.T && N == o.N && K == o.K && out == o.out && det == o.det &&
-           split_req == o.split_req && cus == o.cus;
+           split_req == o.split_req && cus == o.cus && batch == o.batch && wlayout == o.wlayout;
   }
 };
 
@@ -42,6 +46,8 @@ struct Plan {
   int x3;              // BF16x3 router arithmetic
   int out;             // dpg_dtype of the output
   int64_t M, N, K;     // GEMM view: C[M,N] = sum_k A(m,k) B(n,k)
+  int64_t batch;       // problems per launch (the unit stream runs over all of them)
+  int swap_ab;         // weight gradient into a [K,N] output: A is X, B is dY
   int tile;            // index into kTiles
   int fast;            // software-pipelined kernel (gemm_fast.h) instead of the generic one
   int skinny;          // streaming weight-gradient kernel for N <= 128 (skinny_wgrad.h)

@@ -143,6 +143,59 @@ dpg_status dpg_router_wgrad(const float* dy, int64_t lddy, const float* x, int64
                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Batched projection GEMMs: `batch` independent problems of one shape in one
+ * launch, as the page "[Cake 9/13] dense_gemm: batched projection and FP32
+ * router GEMMs" (description) describes for the per-head projections: one
+ * batched BF16 GEMM over strided views, forward and both gradients, with a
+ * choice of weight layout.
+ *   Problem b reads x + b * stride_x (and likewise for every operand; strides in
+ *   elements) and writes its output at y + b * stride_y.  An input stride may be
+ *   0 (the same matrix for every problem); when batch > 1 the outputs must not
+ *   overlap: stacked (stride >= (rows - 1) * ld + cols) or interleaved within
+ *   rows (stride >= cols and (batch - 1) * stride + cols <= ld, e.g. per-head
+ *   views of a token-major buffer), else DPG_ERR_INVALID_ARG.  Every non-zero stride times the element size is a
+ *   multiple of 16 bytes (DPG_ERR_ALIGNMENT).
+ *   w_layout DPG_WEIGHT_NK: the weight is W[N, K] as in the single entry points;
+ *   DPG_WEIGHT_KN: the weight is stored W[K, N] (row stride ldw >= N), i.e. the
+ *   forward is Y = X . W.  For the weight gradient w_layout is the layout of the
+ *   output: dW[N, K] = dY^T X, or dW[K, N] = X^T dY (row stride lddw >= N).
+ *   Everything else (dtypes, alignment, deterministic, split_k, workspace from
+ *   dpg_workspace_size_batched, errors) is as for the single entry points; each
+ *   problem's result equals what the single entry point computes for it under
+ *   the plan the batched call uses.  batch = 0 is a no-op.
+ */
+typedef enum { DPG_WEIGHT_NK = 0, DPG_WEIGHT_KN = 1 } dpg_weight_layout;
+
+dpg_status dpg_forward_batched(const void* x, int64_t ldx, int64_t stride_x,
+                               const void* w, int64_t ldw, int64_t stride_w, dpg_weight_layout w_layout,
+                               void* y, int64_t ldy, int64_t stride_y, dpg_dtype y_dtype,
+                               int64_t batch, int64_t T, int64_t N, int64_t K, int deterministic, int split_k,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+dpg_status dpg_dgrad_batched(const void* dy, int64_t lddy, int64_t stride_dy,
+                             const void* w, int64_t ldw, int64_t stride_w, dpg_weight_layout w_layout,
+                             void* dx, int64_t lddx, int64_t stride_dx, dpg_dtype dx_dtype,
+                             int64_t batch, int64_t T, int64_t N, int64_t K, int deterministic, int split_k,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+dpg_status dpg_wgrad_batched(const void* dy, int64_t lddy, int64_t stride_dy,
+                             const void* x, int64_t ldx, int64_t stride_x,
+                             void* dw, int64_t lddw, int64_t stride_dw, dpg_weight_layout w_layout,
+                             dpg_dtype dw_dtype, int64_t batch, int64_t T, int64_t N, int64_t K,
+                             int deterministic, int split_k,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of a batched call (projection passes 0..2 only; (size_t)-1
+ * for arguments the call would reject). */
+size_t dpg_workspace_size_batched(dpg_pass pass, dpg_weight_layout w_layout, int64_t batch, int64_t T,
+                                  int64_t N, int64_t K, dpg_dtype out_dtype, int deterministic, int split_k);
+
+/* Host-only plan description of a batched call (as dpg_plan_describe). */
+dpg_status dpg_plan_describe_batched(dpg_pass pass, dpg_weight_layout w_layout, int64_t batch, int64_t T,
+                                     int64_t N, int64_t K, dpg_dtype out_dtype, int deterministic, int split_k,
+                                     char* buf, size_t buflen);
+
+/*
  * Bytes of workspace the call with these arguments needs (0 when the plan has a
  * single K split).  For router passes N = E, K = H and out_dtype must be DPG_F32.
  * Returns (size_t)-1 for arguments the matching call would reject.

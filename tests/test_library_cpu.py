@@ -8,6 +8,7 @@ import pytest
 dpg = pytest.importorskip("deterministic_bf16_projection_amd")
 
 L = dpg.lib()
+_i, _p, _c, _z = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 BF16, F32 = dpg.BF16, dpg.F32
 
 
@@ -183,3 +184,46 @@ def test_deterministic_switch_resolution():
         assert len([r for r in rec if "deterministic" in str(r.message)]) == 1
     finally:
         torch.use_deterministic_algorithms(prev)
+
+
+def _plan_b(pass_, batch, T, N, K, out=BF16, det=1, split=0, wl=0):
+    buf = ctypes.create_string_buffer(1024)
+    assert L.dpg_plan_describe_batched(pass_, wl, batch, T, N, K, out, det, split, buf, 1024) == 0
+    return dpg.parse_plan(buf.value.decode())
+
+
+def test_batched_plans():
+    """Batched plans: the unit stream covers every problem, the workspace holds
+    batch x splits planes, the skinny kernel is single-problem only, and a
+    [K,N] weight flips the operand majorness as the GEMM view says."""
+    p = _plan_b(0, 16, 2048, 128, 512)
+    assert p["batch"] == "16" and p["layout"] == "Akmajor_Bkmajor"
+    assert int(p["grid"]) == int(p["tiles"].split("x")[0]) * int(p["tiles"].split("x")[1]) * int(p["splits"]) * 16
+    assert _plan_b(0, 16, 2048, 128, 512, wl=1)["layout"] == "Akmajor_Bmnmajor"
+    assert _plan_b(1, 16, 2048, 128, 512, wl=1)["layout"] == "Akmajor_Bkmajor"
+    q = _plan_b(2, 4, 1025, 64, 512, out=F32, det=0, split=2)
+    assert q["kernel"] != "skinny" and q["splits"] == "2"
+    assert int(q["workspace"]) == 4 * 2 * 64 * 512 * 4
+    assert L.dpg_workspace_size_batched(2, 0, 4, 1025, 64, 512, F32, 0, 2) == 4 * 2 * 64 * 512 * 4
+    r = _plan_b(2, 3, 1025, 64, 512, wl=1)   # dW as [K, N]: M = K, N = N
+    assert r["M"] == "512" and r["N"] == "64"
+    assert _plan_b(2, 1, 16384, 64, 4096)["kernel"] == "skinny"
+    assert _plan_b(0, 0, 64, 64, 64)["kind"] == "noop"
+    buf = ctypes.create_string_buffer(64)
+    assert L.dpg_plan_describe_batched(3, 0, 1, 64, 256, 4096, F32, 1, 0, buf, 64) == 1   # no batched router
+    assert L.dpg_plan_describe_batched(0, 2, 1, 64, 64, 64, BF16, 1, 0, buf, 64) == 1     # bad layout
+
+
+def test_batched_validation_errors():
+    """Rejected before any launch: overlapping batched outputs, misaligned or
+    negative batch strides, bad layouts."""
+    FAKE = 0x10000
+    fwd = L.dpg_forward_batched
+    # x [B,T,K] = [2, 64, 64], w [64, 64], y [2, 64, 64]
+    args = lambda sx, sw, sy, wl=0: (FAKE, 64, sx, FAKE, 64, sw, wl, FAKE, 64, sy, BF16, 2, 64, 64, 64, 1, 0,
+                                     None, 0, None)
+    assert fwd(*args(4096, 0, 64 * 64 - 8)) == 1      # outputs overlap
+    assert fwd(*args(4096, 0, -4096)) == 1            # negative output stride
+    assert fwd(*args(4100, 0, 4096)) == 3             # batch stride not 16-byte aligned
+    assert fwd(*args(4096, 0, 4096, wl=5)) == 1       # bad layout
+    assert fwd(FAKE, 64, 4096, FAKE, 64, 0, 0, FAKE, 64, 4096, BF16, -1, 64, 64, 64, 1, 0, None, 0, None) == 1
