@@ -377,3 +377,26 @@ def test_empty_reductions_write_zeros():
     y = dpg.dpg_forward(torch.empty((0, 64), dtype=torch.bfloat16, device="cuda"),
                         torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda"))
     assert y.shape == (0, 16)
+
+
+# --------------------------------------- leading dimensions of 2^23 and more --
+@pytest.mark.parametrize("pass_name", ["fwd", "dgrad", "wgrad"])
+def test_huge_leading_dimension(pass_name):
+    """Row strides of 2^23 elements and more leave the pipelined and skinny
+    kernels (32-bit tile offsets) for the generic kernel (64-bit addressing);
+    exact-integer inputs, bit for bit."""
+    T, N, K = 5, 64, 256
+    big = (1 << 23) + 64
+    x, w, dy = dpg_inputs.dense(T, N, K, seed_group=11, kind="int")
+    a, b = _operands(pass_name, x, w, dy)
+    ref = _oracle(pass_name, a, b)
+
+    def padded(bits):
+        t = torch.zeros((bits.shape[0], big), dtype=torch.bfloat16, device="cuda")
+        t[:, :bits.shape[1]] = dev_bf16(bits)
+        return t[:, :bits.shape[1]]
+    A, B = padded(a), padded(b)
+    assert A.stride(0) == big and B.stride(0) == big
+    for det, split in [(True, 0), (False, 2)]:
+        out = _run(pass_name, A, B, torch.float32, det=det, split=split)
+        np.testing.assert_array_equal(host_f64(out), ref)
