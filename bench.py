@@ -64,6 +64,16 @@ def read_traffic(kernel_pass):
 
 
 PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def clock_under_load():
+    """Engine clock (GHz) measured with rocm-smi under sustained load of the
+    forward GEMM (committed summary), or None."""
+    path = os.path.join(PROFILE_DIR, "gemm_fwd_4096x12288_T16384_clock_under_load.txt")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"clock_ghz_under_load:\s*([0-9.]+)", open(path).read())
+    return float(m.group(1)) if m else None
 PASS_KERNEL_TAG = {  # template arguments (A K-major, B K-major) of each pass's GEMM kernel
     "fwd": "true, true", "dgrad": "true, false", "wgrad": "false, false"}
 COPY_BYTES = 1 << 30
@@ -92,6 +102,26 @@ def profile_run():
     DW = dpg.dpg_wgrad(DY, X)
     torch.cuda.synchronize()
     print("profile run done", Y.shape, DX.shape, DW.shape)
+
+
+def clock_load(seconds):
+    """The forward GEMM of the benchmark shape in a loop for `seconds` (the
+    engine clock is read meanwhile with rocm-smi)."""
+    import torch
+    import deterministic_bf16_projection_amd as dpg
+    dev = torch.device("cuda:0")
+    X = torch.randn(T_BIG, K_BIG, device=dev).bfloat16()
+    W = (torch.randn(N_BIG, K_BIG, device=dev) * 0.02).bfloat16()
+    Y = torch.empty(T_BIG, N_BIG, device=dev, dtype=torch.bfloat16)
+    t0 = time.time()
+    n = 0
+    while time.time() - t0 < seconds:
+        for _ in range(20):
+            dpg.dpg_forward(X, W, out=Y)
+        torch.cuda.synchronize()
+        n += 20
+    us = (time.time() - t0) * 1e6 / n
+    print("clock load: %d calls, %.1f us per call, %.1f TFLOP/s" % (n, us, 2.0 * T_BIG * N_BIG * K_BIG / us / 1e6))
 
 
 def _read_counter_csv(path):
@@ -324,6 +354,8 @@ def main():
     ap.add_argument("--skip-skinny", action="store_true")
     ap.add_argument("--skip-secondary", action="store_true", help="skip the small, router and step timings")
     ap.add_argument("--profile-run", action="store_true", help="one step + a 1 GiB calibration copy (for rocprofv3)")
+    ap.add_argument("--clock-load", type=float, metavar="SECONDS",
+                    help="run the forward GEMM in a loop for SECONDS (to read the clock under load)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "COMMAND"))
     args = ap.parse_args()
@@ -340,6 +372,9 @@ def main():
 
     if args.profile_run:
         profile_run()
+        return
+    if args.clock_load:
+        clock_load(args.clock_load)
         return
 
     import numpy as np
@@ -402,6 +437,11 @@ def main():
                 "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "algorithmic_flop_per_launch": flop_pass}
+    clk = clock_under_load()
+    if clk:
+        adj = PEAK_BF16_TFLOPS * clk / 2.4
+        roofline["clock_adjusted"] = {"clock_ghz": clk, "peak": round(adj, 1), "frac": round(achieved / adj, 4),
+                                      "source": "rocm-smi sclk under sustained forward-GEMM load (profiles/)"}
 
     skinny = []
     if not args.skip_skinny:
