@@ -357,8 +357,9 @@ dpg_status run(int pass, int wlayout, int64_t batch, const void* a, int64_t lda,
     p.batch_c = sc;
     out_kind = out == DPG_BF16 ? OUT_BF16 : OUT_F32;
   }
-  // the pipelined kernel addresses each tile through 32-bit buffer offsets
-  const bool ld_ok = lda < (1 << 23) && ldb < (1 << 23);
+  // the pipelined kernel addresses each tile through 32-bit buffer offsets: a
+  // K-major tile of 256 rows spans 256 * ld * 2 bytes, below 2^31 for ld < 2^22
+  const bool ld_ok = lda < (1 << 22) && ldb < (1 << 22);
   KernelFn fn = (plan.fast && ld_ok) ? lookup_fast_kernel(plan.tile, plan.layout, out_kind)
                                      : lookup_kernel(plan.tile, plan.layout, plan.x3, out_kind);
   if (!fn) return DPG_ERR_INVALID_ARG;

@@ -137,7 +137,8 @@ struct FastOperand {
 };
 
 // Buffer descriptor of the K tile starting at k0 (32-bit arithmetic only: the
-// launcher guarantees ld < 2^23, so one tile spans less than 2^31 bytes).
+// launcher guarantees ld < 2^22, so one tile of at most 256 rows of BF16, or
+// 128 rows of FP32, spans less than 2^31 bytes).
 //  K-major (element (row, k) at ptr[row * ld + k]): rows [row0, rows), k < K.
 //  MN-major (element (row, k) at ptr[k * ld + row]): reduction rows
 //  [k0, min(K, k0 + 64)), columns [row0, rows) of each.

@@ -379,14 +379,15 @@ def test_empty_reductions_write_zeros():
     assert y.shape == (0, 16)
 
 
-# --------------------------------------- leading dimensions of 2^23 and more --
+# --------------------------------------- leading dimensions of 2^22 and more --
 @pytest.mark.parametrize("pass_name", ["fwd", "dgrad", "wgrad"])
-def test_huge_leading_dimension(pass_name):
-    """Row strides of 2^23 elements and more leave the pipelined and skinny
-    kernels (32-bit tile offsets) for the generic kernel (64-bit addressing);
-    exact-integer inputs, bit for bit."""
+@pytest.mark.parametrize("log2_ld", [22, 23])
+def test_huge_leading_dimension(pass_name, log2_ld):
+    """Row strides of 2^22 elements and more leave the pipelined kernel, and
+    of 2^23 and more the skinny kernel (32-bit tile offsets), for the generic
+    kernel (64-bit addressing); exact-integer inputs, bit for bit."""
     T, N, K = 5, 64, 256
-    big = (1 << 23) + 64
+    big = (1 << log2_ld) + 64
     x, w, dy = dpg_inputs.dense(T, N, K, seed_group=11, kind="int")
     a, b = _operands(pass_name, x, w, dy)
     ref = _oracle(pass_name, a, b)
