@@ -56,7 +56,8 @@ KernelFn lookup_kernel(int tile, int layout, int x3, int out_kind) {
   return table[tile][layout][x3][out_kind];
 }
 
-// software-pipelined kernels for the 256x256 and 128x128 tiles
+// software-pipelined kernels for the 256x256 and 128x128 tiles (BF16x3: the
+// 128x128 tile, FP32 or partial output)
 template <int BM, int BN, int WM_, int WN_, int LAYOUT>
 struct FastRow {
   static constexpr KernelFn fns[3] = {
@@ -65,7 +66,15 @@ struct FastRow {
       &gemm_fast_kernel<BM, BN, WM_, WN_, LAYOUT != LAYOUT_WGRAD, LAYOUT == LAYOUT_FWD, OUT_PARTIAL>};
 };
 
-KernelFn lookup_fast_kernel(int tile, int layout, int out_kind) {
+template <int LAYOUT>
+struct FastRowX3 {
+  static constexpr KernelFn fns[3] = {
+      nullptr,
+      &gemm_fast_kernel<128, 128, 2, 2, LAYOUT != LAYOUT_WGRAD, LAYOUT == LAYOUT_FWD, OUT_F32, true>,
+      &gemm_fast_kernel<128, 128, 2, 2, LAYOUT != LAYOUT_WGRAD, LAYOUT == LAYOUT_FWD, OUT_PARTIAL, true>};
+};
+
+KernelFn lookup_fast_kernel(int tile, int layout, int x3, int out_kind) {
 #define DPG_FROW(BM, BN, WM_, WN_, L) \
   {FastRow<BM, BN, WM_, WN_, L>::fns[0], FastRow<BM, BN, WM_, WN_, L>::fns[1], FastRow<BM, BN, WM_, WN_, L>::fns[2]}
   static const KernelFn table[2][3][3] = {
@@ -73,6 +82,13 @@ KernelFn lookup_fast_kernel(int tile, int layout, int out_kind) {
       {DPG_FROW(128, 128, 2, 2, 0), DPG_FROW(128, 128, 2, 2, 1), DPG_FROW(128, 128, 2, 2, 2)},
   };
 #undef DPG_FROW
+  static const KernelFn table_x3[3][3] = {
+      {FastRowX3<0>::fns[0], FastRowX3<0>::fns[1], FastRowX3<0>::fns[2]},
+      {FastRowX3<1>::fns[0], FastRowX3<1>::fns[1], FastRowX3<1>::fns[2]},
+      {FastRowX3<2>::fns[0], FastRowX3<2>::fns[1], FastRowX3<2>::fns[2]},
+  };
+  if (layout < 0 || layout > 2 || out_kind < 0 || out_kind > 2) return nullptr;
+  if (x3) return tile == 1 ? table_x3[layout][out_kind] : nullptr;
   if (tile < 0 || tile > 1) return nullptr;
   return table[tile][layout][out_kind];
 }
@@ -360,7 +376,7 @@ dpg_status run(int pass, int wlayout, int64_t batch, const void* a, int64_t lda,
   // the pipelined kernel addresses each tile through 32-bit buffer offsets: a
   // K-major tile of 256 rows spans 256 * ld * 2 bytes, below 2^31 for ld < 2^22
   const bool ld_ok = lda < (1 << 22) && ldb < (1 << 22);
-  KernelFn fn = (plan.fast && ld_ok) ? lookup_fast_kernel(plan.tile, plan.layout, out_kind)
+  KernelFn fn = (plan.fast && ld_ok) ? lookup_fast_kernel(plan.tile, plan.layout, plan.x3, out_kind)
                                      : lookup_kernel(plan.tile, plan.layout, plan.x3, out_kind);
   if (!fn) return DPG_ERR_INVALID_ARG;
   void* args[] = {&p};
@@ -368,7 +384,9 @@ dpg_status run(int pass, int wlayout, int64_t batch, const void* a, int64_t lda,
   const int threads = (fast && plan.tile == 0) ? 512 : tile_threads(plan.tile);
   // the pipelined kernel is persistent: one workgroup per CU slot walks its units
   int64_t grid = plan.skinny ? (int64_t)plan.tiles_m * plan.tiles_n * plan.splits : plan.grid;
-  if (fast) grid = std::min<int64_t>(grid, (int64_t)device_cus() * (plan.tile == 0 ? 1 : 2));
+  // (one workgroup per CU for the 256x256 tile and for BF16x3, whose two hi/lo
+  // planes fill the LDS; two for the BF16 128x128 tile)
+  if (fast) grid = std::min<int64_t>(grid, (int64_t)device_cus() * ((plan.tile == 0 || plan.x3) ? 1 : 2));
   hipError_t e = hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3(threads), args, 0, stream);
   if (e != hipSuccess) return DPG_ERR_HIP;
   if (plan.splits > 1) return launch_reduce(plan, ws, c, ldc, sc, out, stream);

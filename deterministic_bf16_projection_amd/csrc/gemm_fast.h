@@ -76,6 +76,7 @@ struct FastOperand {
   static_assert(NT == 256 && (KMAJ || R <= NT), "one block per thread, 32 rows per K-major load");
   static constexpr int LOADS = KMAJ ? R * 8 / NT : 8;
   static constexpr int BLOCK_THREADS = KMAJ ? NT : R;  // threads that own data
+  static constexpr int NLOADS = LOADS, NWRITES = LOADS;  // per K tile (scheduling)
   u32x4 g[LOADS];
   // Load i reads at voff0 + i * vstep bytes, and LDS slot i goes to lds0 with
   // a per-slot constant (added for K-major, XORed for MN-major).
@@ -118,7 +119,7 @@ struct FastOperand {
     for (int i = 0; i < LOADS; ++i) g[i] = buf_load16(r, v + (uint32_t)i * vstep);
   }
 
-  __device__ __forceinline__ void store(__bf16* plane) const {
+  __device__ __forceinline__ void store(__bf16* plane, __bf16* /*lo plane: BF16x3 only*/ = nullptr) const {
     if (BLOCK_THREADS < NT && !owner) return;
     int o = lds0;
     // MN-major: form the eight slot offsets here rather than in the loop
@@ -136,28 +137,117 @@ struct FastOperand {
   }
 };
 
+// BF16x3 operand: an FP32 source split while staging into hi = bf16(a) and
+// lo = bf16(a - hi) (round to nearest even), written to two BF16 planes with
+// FastOperand's LDS layout.  K-major: each thread stages whole 8-element
+// chunks (two 16-byte loads each) of rows tid / 8 + 32 i.  MN-major: one 8x8
+// block (8 reduction rows x 8 output rows, sixteen 16-byte loads) per thread
+// for the first R threads, with FastOperand's lane numbering; the transpose of
+// FP32 values is a renaming of registers, and lanes with (mb / 8) odd take
+// column m ^ 1 into slot m by a per-lane select.
+template <int R, bool KMAJ, int NT>
+struct FastOperandX3 {
+  static_assert(NT == 256 && R <= NT && (KMAJ || R % 8 == 0), "one block per thread, 32 rows per K-major chunk");
+  static constexpr int CHUNKS = KMAJ ? R * 8 / NT : 1;  // K-major chunks per thread
+  static constexpr int LOADS = KMAJ ? 2 * CHUNKS : 16;
+  static constexpr int BLOCK_THREADS = KMAJ ? NT : R;
+  static constexpr int NLOADS = LOADS, NWRITES = KMAJ ? 2 * CHUNKS : 16;
+  u32x4 g[LOADS];
+  uint32_t voff0, vstep;
+  int lds0;
+  int flip;
+  bool owner;
+
+  __device__ __forceinline__ void init(int tid, int64_t ld) {
+    owner = tid < BLOCK_THREADS;
+    if (KMAJ) {
+      const int c = tid & 7, r = tid >> 3;
+      voff0 = (uint32_t)((r * ld + c * 8) * 4);
+      vstep = (uint32_t)(32 * ld * 4);
+      lds0 = lds_chunk_off(r, c);
+      flip = 0;
+    } else {
+      const int mb = tid % (R / 8), kc = (tid / (R / 8)) & 7;
+      flip = (mb >> 3) & 1;
+      voff0 = (uint32_t)((kc * 8 * ld + mb * 8) * 4);
+      vstep = (uint32_t)(ld * 4);
+      lds0 = (mb * 512) | ((((9 * flip) ^ ((kc ^ mb) & 7))) << 3);
+    }
+  }
+
+  __device__ __forceinline__ void load(rsrc_t r) {
+    if (BLOCK_THREADS < NT && !owner) return;
+    const uint32_t v = voff0;
+    if constexpr (KMAJ) {
+#pragma unroll
+      for (int i = 0; i < CHUNKS; ++i) {
+        g[2 * i] = buf_load16(r, v + (uint32_t)i * vstep);
+        g[2 * i + 1] = buf_load16(r, v + (uint32_t)i * vstep + 16u);
+      }
+    } else {
+#pragma unroll
+      for (int l = 0; l < 8; ++l) {
+        g[2 * l] = buf_load16(r, v + (uint32_t)l * vstep);
+        g[2 * l + 1] = buf_load16(r, v + (uint32_t)l * vstep + 16u);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void store(__bf16* hi_plane, __bf16* lo_plane) const {
+    if (BLOCK_THREADS < NT && !owner) return;
+    int o = lds0;
+    asm volatile("" : "+v"(o));
+    if constexpr (KMAJ) {
+#pragma unroll
+      for (int i = 0; i < CHUNKS; ++i) {
+        u32x4 hi, lo;
+        split3_x8(__builtin_bit_cast(f32x4, g[2 * i]), __builtin_bit_cast(f32x4, g[2 * i + 1]), hi, lo);
+        const int off = ((i & 1) ? (o ^ 32) : o) + 2048 * i;
+        *(u32x4*)(hi_plane + off) = hi;
+        *(u32x4*)(lo_plane + off) = lo;
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        // column m ^ flip of the block: element j = m ^ flip of each row's 8 values
+        float f[8];
+#pragma unroll
+        for (int l = 0; l < 8; ++l) {
+          const u32x4 q = g[2 * l + (m >> 2)];
+          const uint32_t a = q[m & 3], b = q[(m & 3) ^ 1];
+          f[l] = __builtin_bit_cast(float, flip ? b : a);
+        }
+        u32x4 hi, lo;
+        split3_x8(f32x4{f[0], f[1], f[2], f[3]}, f32x4{f[4], f[5], f[6], f[7]}, hi, lo);
+        *(u32x4*)(hi_plane + (o ^ (72 * m))) = hi;
+        *(u32x4*)(lo_plane + (o ^ (72 * m))) = lo;
+      }
+    }
+  }
+};
+
 // Buffer descriptor of the K tile starting at k0 (32-bit arithmetic only: the
 // launcher guarantees ld < 2^22, so one tile of at most 256 rows of BF16, or
 // 128 rows of FP32, spans less than 2^31 bytes).
 //  K-major (element (row, k) at ptr[row * ld + k]): rows [row0, rows), k < K.
 //  MN-major (element (row, k) at ptr[k * ld + row]): reduction rows
 //  [k0, min(K, k0 + 64)), columns [row0, rows) of each.
-template <bool KMAJ>
-__device__ __forceinline__ rsrc_t tile_rsrc(const __bf16* ptr, int ld, int row0, int rows, int k0, int K) {
+template <bool KMAJ, int TILE_ROWS = 256, class T>
+__device__ __forceinline__ rsrc_t tile_rsrc(const T* ptr, int ld, int row0, int rows, int k0, int K) {
   int bytes;
-  const __bf16* base;
+  const T* base;
   if (KMAJ) {
-    const int valid = min(rows - row0, 256);
-    bytes = ((valid - 1) * ld + (K - k0)) * 2;
+    const int valid = min(rows - row0, TILE_ROWS);
+    bytes = ((valid - 1) * ld + (K - k0)) * (int)sizeof(T);
     base = ptr + (int64_t)row0 * ld + k0;
   } else {
     const int kr = min(K - k0, 64);
-    bytes = ((kr - 1) * ld + (rows - row0)) * 2;
+    bytes = ((kr - 1) * ld + (rows - row0)) * (int)sizeof(T);
     bytes = kr > 0 ? bytes : 0;
     base = ptr + (int64_t)k0 * ld + row0;
   }
   bytes = max(bytes, 0);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(base), (short)0, bytes, 0x00020000);
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(base), (short)0, bytes, 0x00020000);
 }
 
 // Scheduling groups: MFMA, DS read, DS write, VMEM read.
@@ -248,17 +338,22 @@ __device__ __forceinline__ bool cursor_valid(const UnitMap& m, const StepCursor&
 // (eight-wave tiles: waves 0-3 stage A, waves 4-7 stage B).
 enum StageRole { ROLE_BOTH = 0, ROLE_A = 1, ROLE_B = 2 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KMAJ, bool B_KMAJ, int OUT, int ROLE>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KMAJ, bool B_KMAJ, int OUT, int ROLE, bool X3 = false>
 struct FastGemm {
   static constexpr int BK = 64;
   static constexpr int NT = 64 * WAVES_M * WAVES_N;
   static constexpr int NTL = ROLE == ROLE_BOTH ? NT : NT / 2;  // threads staging one operand
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static_assert(WM % 64 == 0 && WN % 64 == 0, "fragment swizzle parity follows the fragment index");
+  static_assert(!X3 || ROLE == ROLE_BOTH, "BF16x3 runs on the four-wave tile");
   static constexpr int FM = WM / 32, FN = WN / 32;
-  static constexpr int PLANE_A = BM * BK, PLANE_B = BN * BK, STAGE = PLANE_A + PLANE_B;
-  typedef FastOperand<BM, A_KMAJ, NTL> OpA;
-  typedef FastOperand<BN, B_KMAJ, NTL> OpB;
+  // BF16x3: every operand has a hi and a lo plane (A hi, A lo, B hi, B lo)
+  static constexpr int PLANES = X3 ? 2 : 1;
+  static constexpr int PLANE_A = BM * BK, PLANE_B = BN * BK, STAGE = (PLANE_A + PLANE_B) * PLANES;
+  static constexpr int B_BASE = PLANE_A * PLANES;  // first B plane in a stage
+  typedef typename std::conditional<X3, float, __bf16>::type InT;
+  typedef typename std::conditional<X3, FastOperandX3<BM, A_KMAJ, NTL>, FastOperand<BM, A_KMAJ, NTL>>::type OpA;
+  typedef typename std::conditional<X3, FastOperandX3<BN, B_KMAJ, NTL>, FastOperand<BN, B_KMAJ, NTL>>::type OpB;
   static constexpr bool DO_A = ROLE != ROLE_B, DO_B = ROLE != ROLE_A;
 
   // Accumulators hold the transposed product: acc[i][j] is the 32x32 block
@@ -297,8 +392,8 @@ struct FastGemm {
   }
 
   static __device__ __forceinline__ void run(__bf16* smem, const GemmParams& p, int ltid, int lane, int wm, int wn) {
-    const __bf16* A = (const __bf16*)p.a;
-    const __bf16* B = (const __bf16*)p.b;
+    const InT* A = (const InT*)p.a;
+    const InT* B = (const InT*)p.b;
     const int lda = (int)p.lda, ldb = (int)p.ldb;
     const UnitMap um = {p.tiles_m, p.tiles_n, p.group_m, p.splits, p.kt_per_split, p.kt_total,
                         p.tiles_m * p.tiles_n * p.splits * p.batch, p.tiles_m * p.tiles_n * p.splits};
@@ -326,37 +421,53 @@ struct FastGemm {
 #pragma unroll
     for (int i = 0; i < FM; ++i) a_row[i] = (wm * WM + i * 32 + lr) * 64;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) b_row[j] = PLANE_A + (wn * WN + j * 32 + lr) * 64;
+    for (int j = 0; j < FN; ++j) b_row[j] = B_BASE + (wn * WN + j * 32 + lr) * 64;
     int koff[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) koff[s] = ((2 * s + lh) ^ sw) << 3;
 
     bf16x8 fa[2][FM], fb[2][FN];
-    // fragments of k-step S (0..3) of a stage into buffer BUF
+    bf16x8 fal[2][FM], fbl[2][FN];  // BF16x3 lo fragments
+    // fragments of k-step S (0..3) of a stage into buffer BUF (hi and, for
+    // BF16x3, lo planes)
 #define DPG_READ_FRAGS(stage, S, BUF)                                                                      \
   do {                                                                                                     \
-    _Pragma("unroll") for (int i = 0; i < FM; ++i) fa[BUF][i] =                                            \
-        as_bf16x8(*(const u32x4*)((stage) + a_row[i] + koff[(S) ^ (2 * (i & 1))]));                       \
-    _Pragma("unroll") for (int j = 0; j < FN; ++j) fb[BUF][j] =                                            \
-        as_bf16x8(*(const u32x4*)((stage) + b_row[j] + koff[(S) ^ (2 * (j & 1))]));                       \
+    _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                                       \
+      fa[BUF][i] = as_bf16x8(*(const u32x4*)((stage) + a_row[i] + koff[(S) ^ (2 * (i & 1))]));             \
+      if constexpr (X3)                                                                                    \
+        fal[BUF][i] = as_bf16x8(*(const u32x4*)((stage) + PLANE_A + a_row[i] + koff[(S) ^ (2 * (i & 1))])); \
+    }                                                                                                      \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                                       \
+      fb[BUF][j] = as_bf16x8(*(const u32x4*)((stage) + b_row[j] + koff[(S) ^ (2 * (j & 1))]));             \
+      if constexpr (X3)                                                                                    \
+        fbl[BUF][j] = as_bf16x8(*(const u32x4*)((stage) + PLANE_B + b_row[j] + koff[(S) ^ (2 * (j & 1))])); \
+    }                                                                                                      \
   } while (0)
-    // MFMAs of rows [I0, I1) of the wave tile from fragment buffer BUF
+    // MFMAs of rows [I0, I1) of the wave tile from fragment buffer BUF; BF16x3
+    // adds lo*hi, hi*lo, hi*hi in that order into each accumulator
 #define DPG_MFMAS(BUF, I0, I1)                                                                             \
   do {                                                                                                     \
-    _Pragma("unroll") for (int i = (I0); i < (I1); ++i) _Pragma("unroll") for (int j = 0; j < FN; ++j)     \
-        acc[i][j] = mfma32(fb[BUF][j], fa[BUF][i], acc[i][j]);                                             \
+    _Pragma("unroll") for (int i = (I0); i < (I1); ++i) _Pragma("unroll") for (int j = 0; j < FN; ++j) {   \
+      if constexpr (X3) {                                                                                  \
+        acc[i][j] = mfma32(fb[BUF][j], fal[BUF][i], acc[i][j]);                                            \
+        acc[i][j] = mfma32(fbl[BUF][j], fa[BUF][i], acc[i][j]);                                            \
+      }                                                                                                    \
+      acc[i][j] = mfma32(fb[BUF][j], fa[BUF][i], acc[i][j]);                                               \
+    }                                                                                                      \
   } while (0)
     // loads of the step at cursor L (out-of-range steps read nothing)
     auto load = [&](const StepCursor& L) {
       // a step past the last unit gets empty descriptors (one row, no K left)
       const bool ok = cursor_valid(um, L);
       const int kk = ok ? (L.kt0 + L.kt) * BK : p.K;
-      if (DO_A) opa.load(tile_rsrc<A_KMAJ>(A + L.b * p.batch_a, lda, L.row0, ok ? p.M : L.row0 + 1, kk, p.K));
-      if (DO_B) opb.load(tile_rsrc<B_KMAJ>(B + L.b * p.batch_b, ldb, L.col0, ok ? p.N : L.col0 + 1, kk, p.K));
+      if (DO_A)
+        opa.load(tile_rsrc<A_KMAJ, BM>(A + L.b * p.batch_a, lda, L.row0, ok ? p.M : L.row0 + 1, kk, p.K));
+      if (DO_B)
+        opb.load(tile_rsrc<B_KMAJ, BN>(B + L.b * p.batch_b, ldb, L.col0, ok ? p.N : L.col0 + 1, kk, p.K));
     };
     auto store = [&](__bf16* stage) {
-      if (DO_A) opa.store(stage);
-      if (DO_B) opb.store(stage + PLANE_A);
+      if (DO_A) opa.store(stage, stage + PLANE_A);
+      if (DO_B) opb.store(stage + B_BASE, stage + B_BASE + PLANE_B);
     };
 
     StepCursor C = cursor_at<BM, BN>(um, blockIdx.x);
@@ -370,10 +481,10 @@ struct FastGemm {
     __syncthreads();
     DPG_READ_FRAGS(smem, 0, 0);
 
-    constexpr int NM = FM * FN;  // MFMAs per k-step
-    constexpr int NR = FM + FN;  // fragment reads per k-step
-    constexpr int NW = (DO_A ? OpA::LOADS : 0) + (DO_B ? OpB::LOADS : 0);  // LDS writes per tile
-    constexpr int NV = NW;                                                 // buffer loads per tile
+    constexpr int NM = FM * FN * (X3 ? 3 : 1);  // MFMAs per k-step
+    constexpr int NR = (FM + FN) * PLANES;        // fragment reads per k-step
+    constexpr int NW = (DO_A ? OpA::NWRITES : 0) + (DO_B ? OpB::NWRITES : 0);  // LDS writes per tile
+    constexpr int NV = (DO_A ? OpA::NLOADS : 0) + (DO_B ? OpB::NLOADS : 0);    // buffer loads per tile
     for (int it = 0; cursor_valid(um, C); ++it) {
       const __bf16* cur = smem + (it & 1) * STAGE;
       __bf16* nxt = smem + ((it + 1) & 1) * STAGE;
@@ -433,12 +544,13 @@ struct FastGemm {
   }
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KMAJ, bool B_KMAJ, int OUT>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KMAJ, bool B_KMAJ, int OUT, bool X3 = false>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_fast_kernel(GemmParams p) {
   constexpr int BK = 64;
   constexpr int NT = 64 * WAVES_M * WAVES_N;
   static_assert(NT == 256 || NT == 512, "four or eight waves");
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (BM + BN) * BK];
+  static_assert(!X3 || NT == 256, "BF16x3 runs on the four-wave tile");
+  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * (BM + BN) * BK * (X3 ? 2 : 1)];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: SGPR
@@ -449,7 +561,7 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_fast_kernel(Ge
     else
       FastGemm<BM, BN, WAVES_M, WAVES_N, A_KMAJ, B_KMAJ, OUT, ROLE_B>::run(smem, p, tid - 256, lane, wm, wn);
   } else {
-    FastGemm<BM, BN, WAVES_M, WAVES_N, A_KMAJ, B_KMAJ, OUT, ROLE_BOTH>::run(smem, p, tid, lane, wm, wn);
+    FastGemm<BM, BN, WAVES_M, WAVES_N, A_KMAJ, B_KMAJ, OUT, ROLE_BOTH, X3>::run(smem, p, tid, lane, wm, wn);
   }
 }
 

@@ -10,13 +10,13 @@ namespace dpg {
 
 // Rates are per CU, shared by the workgroups resident on it (measured on
 // MI355X: one 64x64 workgroup already sustains most of what a CU gives that
-// kernel).  BF16x3 plans use the 64x64 tile only (the larger generic tiles run
-// the three-product loop slower per CU).
+// kernel).  BF16x3 plans use the pipelined 128x128 tile or the generic 64x64
+// one.
 const TileShape kTiles[kNumTiles] = {
-    // bm, bn, bk, threads, occupancy, eff, x3_eff, x3_ok, fast_ok
-    {256, 256, 64, 256, 1, 0.55, 0.0, false, true},
-    {128, 128, 64, 256, 2, 0.36, 0.0, false, true},
-    {64, 64, 64, 256, 4, 0.20, 0.19, true, false},
+    // bm, bn, bk, threads, occupancy, eff, x3_eff, x3_occupancy, x3_ok, fast_ok
+    {256, 256, 64, 256, 1, 0.55, 0.0, 0, false, true},
+    {128, 128, 64, 256, 2, 0.36, 0.28, 1, true, true},
+    {64, 64, 64, 256, 4, 0.20, 0.19, 2, true, false},
 };
 
 namespace {
@@ -71,7 +71,7 @@ double estimate_us(const TileShape& ts, bool fast, int64_t batch, int64_t M, int
   s = cdiv(kt_total, kt_per);  // no empty splits
   const int64_t units = tiles * s;
   const double flop_unit = 2.0 * ts.bm * ts.bn * (double)(kt_per * ts.bk) * (x3 ? 3 : 1);
-  const int64_t occ_used = std::min<int64_t>(ts.occupancy, cdiv(units, cus));
+  const int64_t occ_used = std::min<int64_t>(x3 ? ts.x3_occupancy : ts.occupancy, cdiv(units, cus));
   const int64_t rounds = cdiv(units, (int64_t)cus * occ_used);
   const double cu_rate = kCuFlops * (x3 ? ts.x3_eff : ts.eff);
   const double epi_us = (double)occ_used * ts.bm * ts.bn * (s > 1 ? 4 : out_bytes) / kCuStore * 1e6;
@@ -151,7 +151,7 @@ bool make_plan(const PlanKey& key, Plan* p) {
     for (int sc : kSplitChoices) {
       if (key.split_req != 0 && sc != key.split_req) continue;
       int s, ktp;
-      const bool fast = !p->x3 && ts.fast_ok && (p->layout == LAYOUT_WGRAD || p->K % 64 == 0);
+      const bool fast = ts.fast_ok && (p->layout == LAYOUT_WGRAD || p->K % 64 == 0);
       const double t =
           estimate_us(ts, fast, p->batch, p->M, p->N, p->K, p->x3, out_bytes, in_bytes, sc, key.cus, &s, &ktp);
       if (t < best * 0.97) {  // prefer the earlier (larger tile, fewer splits) choice unless 3% faster
@@ -170,7 +170,7 @@ bool make_plan(const PlanKey& key, Plan* p) {
   p->group_m = std::min(p->tiles_m, 8);
   // the pipelined kernel needs whole 64-wide K tiles on K-major operands
   const bool kmajor_ok = p->layout == LAYOUT_WGRAD || (p->K % 64) == 0;
-  p->fast = (!p->x3 && ts.fast_ok && kmajor_ok) ? 1 : 0;
+  p->fast = (ts.fast_ok && kmajor_ok) ? 1 : 0;
   p->grid = (int64_t)p->tiles_m * p->tiles_n * p->splits * p->batch;
   p->ws_bytes = p->splits > 1 ? (size_t)p->batch * p->splits * (size_t)p->M * (size_t)p->N * 4u : 0;
   p->est_us = best;

@@ -175,6 +175,29 @@ def test_router_exact_bf16x3(op, det, split):
     np.testing.assert_array_equal(host_f64(out), orc(a, b, mode="bf16x3"))
 
 
+@pytest.mark.parametrize("op", ["fwd", "dgrad", "wgrad"])
+@pytest.mark.parametrize("det,split", [(True, 0), (False, 3)])
+def test_router_exact_bf16x3_pipelined(op, det, split):
+    """T = H = 4096: every router pass runs the pipelined BF16x3 kernel
+    (128x128 tiles, hi/lo planes split while staging); a = hi + lo inputs make
+    the three-product sum exact, so sampled outputs equal the oracle's BF16x3
+    value bit for bit."""
+    T, E, H = 4096, 256, 4096
+    x, w, dy = dpg_inputs.router(T, E, H, seed_group=12, kind="exact")
+    pass_id = {"fwd": 3, "dgrad": 4, "wgrad": 5}[op]
+    plan = dpg.parse_plan(dpg.plan_describe(pass_id, T, E, H, torch.float32, det, split))
+    assert plan["kernel"] == "pipelined" and plan["x3"] == "1", plan
+    fn = {"fwd": dpg.dpg_router_forward, "dgrad": dpg.dpg_router_dgrad, "wgrad": dpg.dpg_router_wgrad}[op]
+    orc = {"fwd": oracle.forward, "dgrad": oracle.dgrad, "wgrad": oracle.wgrad}[op]
+    a, b = {"fwd": (x, w), "dgrad": (dy, w), "wgrad": (dy, x)}[op]
+    out = fn(dev_f32(a), dev_f32(b), deterministic=det, split_k=split)
+    torch.cuda.synchronize()
+    rows, cols = out.shape
+    ii, jj = sample_positions(rows, cols, 3000, seed=7)
+    ref = orc(a, b, mode="bf16x3", rows=ii, cols=jj)
+    np.testing.assert_array_equal(host_f64(out)[ii, jj], ref)
+
+
 # ----------------------------------------- projection 4096 -> 12288, full size --
 @pytest.fixture(scope="module")
 def big_inputs():
