@@ -372,18 +372,36 @@ struct FastGemm {
     }
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
+      // lanes l and l + 32 hold the same row, so the checks below never split a pair
       const int m = c.row0 + wm * WM + i * 32 + (lane & 31);
       if (m >= p.M) continue;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
+        if constexpr (OUT == OUT_BF16) {
+          // Columns 16 h + [0, 16) of the block: lane l (< 32) holds 16 h + [0, 4)
+          // (group 2h) and 16 h + [8, 12) (group 2h + 1), lane l + 32 the next
+          // four of each.  Swapping group 2h of the upper lanes with group 2h + 1
+          // of the lower lanes leaves lane l with 16 h + [0, 8) and lane l + 32
+          // with 16 h + [8, 16): one 16-byte store each.
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int n = c.col0 + wn * WN + j * 32 + q * 8 + (lane >> 5) * 4;
-          if (n >= p.N) continue;
-          const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
-          if (OUT == OUT_BF16) {
-            *(u32x2*)(out + ((int64_t)m * ldc + n) * 2) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
-          } else {
+          for (int h = 0; h < 2; ++h) {
+            const int q0 = 2 * h, q1 = 2 * h + 1;
+            const uint32_t x0 = pack_bf16x2(acc[i][j][4 * q0], acc[i][j][4 * q0 + 1]);
+            const uint32_t x1 = pack_bf16x2(acc[i][j][4 * q0 + 2], acc[i][j][4 * q0 + 3]);
+            const uint32_t y0 = pack_bf16x2(acc[i][j][4 * q1], acc[i][j][4 * q1 + 1]);
+            const uint32_t y1 = pack_bf16x2(acc[i][j][4 * q1 + 2], acc[i][j][4 * q1 + 3]);
+            const auto s0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+            const int n = c.col0 + wn * WN + j * 32 + h * 16 + (lane >> 5) * 8;
+            if (n >= p.N) continue;
+            *(u32x4*)(out + ((int64_t)m * ldc + n) * 2) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int n = c.col0 + wn * WN + j * 32 + q * 8 + (lane >> 5) * 4;
+            if (n >= p.N) continue;
+            const f32x4 v = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
             *(f32x4*)(out + ((int64_t)m * ldc + n) * 4) = v;
           }
         }
