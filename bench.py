@@ -210,7 +210,7 @@ def summarize_trace(stats_csv, command, out_name="bench_4096x12288_T16384_kernel
     print("wrote", path)
 
 
-def cpu_baseline(target_s=12.0):
+def cpu_baseline(target_s=20.0):
     """The FP64 oracle as it stands, on a bounded sample of the same workload:
     the forward pass's first R rows of Y[16384, 12288] (all columns)."""
     import numpy as np
