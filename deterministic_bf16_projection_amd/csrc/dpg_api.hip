@@ -308,6 +308,8 @@ dpg_status run(int pass, int wlayout, int64_t batch, const void* a, int64_t lda,
     return e == hipSuccess ? DPG_OK : DPG_ERR_HIP;
   }
 
+  // the skinny kernel's 64-token tiles span at most 64 * ld * 2 bytes of 32-bit
+  // buffer offsets (below 2^31 for ld < 2^23); larger strides take the generic kernel
   if (plan.skinny && lda < (1 << 23) && ldb < (1 << 23)) {
     SkinnyParams q;
     q.dy = a;

@@ -26,6 +26,9 @@
  *   (its number of columns) is a multiple of 8 elements.  Otherwise the call
  *   returns DPG_ERR_ALIGNMENT.  T (the row count of X, dY, Y and dX) may be any
  *   value >= 0, including odd counts of 64-token blocks.
+ * - Row strides of 2^22 elements or more are supported; such calls run a
+ *   slower kernel with 64-bit addressing (the pipelined kernels address a tile
+ *   through 32-bit buffer offsets).
  * - Outputs are written only in [rows, cols]; elements of a padded row beyond
  *   `cols` are never touched.  Outputs are overwritten, never read.
  * - An empty output (a zero extent) is a no-op.  An empty reduction (K = 0 for
