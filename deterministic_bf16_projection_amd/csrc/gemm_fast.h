@@ -1,5 +1,6 @@
-// Software-pipelined BF16 MFMA GEMM for gfx950 (the path of the large
-// projection passes).  C[M,N] = sum_k A(m,k) * B(n,k), FP32 accumulation.
+// Software-pipelined MFMA GEMM for gfx950 (the path of the large projection
+// passes and of the BF16x3 router from about a thousand tokens up).
+// C[M,N] = sum_k A(m,k) * B(n,k), FP32 accumulation.
 //
 // Compared with the generic kernel in gemm_kernel.h:
 // * Operands are fetched with raw buffer loads.  The buffer descriptor of each
@@ -7,18 +8,23 @@
 //   the matrix end and reduction rows past K read as zero in hardware: the main
 //   loop has no branches.
 // * MN-major operands (input gradient B, both weight-gradient operands) are
-//   transposed in registers (8x8 blocks of BF16 through v_perm_b32) on their
-//   way to LDS, so LDS always holds K-contiguous rows and every MFMA fragment
-//   is one ds_read_b128.
+//   transposed in registers (8x8 blocks of BF16 through v_perm_b32, or of FP32
+//   by renaming) on their way to LDS, so LDS always holds K-contiguous rows and
+//   every MFMA fragment is one ds_read_b128.  Consecutive lanes read
+//   consecutive 16-byte chunks of one global row.
 // * LDS rows are 64 BF16 (128 B) with 16-byte chunks XOR-swizzled per row.
 // * Per K tile (64) each wave runs 4 k-steps of 16; the fragments of step s+1
 //   are read while the MFMAs of step s issue, the global loads of the tile
 //   after next are issued right after the staged registers are written to the
 //   other LDS stage, and the single barrier per tile sits in the middle of the
 //   last step's MFMAs.
-// Requirements (checked by the planner): K-major operands have K % 64 == 0;
-// all contiguous extents are multiples of 8 elements; operand spans fit the
-// 32-bit buffer range.
+// * The grid is persistent: each workgroup walks a stream of (problem, tile,
+//   K split) units with the K pipeline running across unit boundaries.
+// * BF16x3 (FP32 operands): hi and lo BF16 planes per operand, split while
+//   staging; each k-step adds lo*hi, hi*lo, hi*hi into one accumulator.
+// Requirements: K-major operands have K % 64 == 0 (planner); all contiguous
+// extents are multiples of 8 elements; row strides below 2^22 elements so a
+// tile spans less than 2^31 bytes of buffer offsets (launcher).
 #pragma once
 #include "device_common.h"
 #include "gemm_kernel.h"
@@ -27,11 +33,6 @@
 namespace dpg {
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
-  const int64_t clamped = bytes < 0 ? 0 : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFll : bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)(uint32_t)clamped, 0x00020000);
-}
 
 __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, 0);
