@@ -227,6 +227,41 @@ struct FastOperandX3 {
   }
 };
 
+// K-major operand fetched straight into LDS (buffer_load ... lds): each
+// instruction moves 64 lanes x 16 B into 1 KB of consecutive LDS, i.e. 8 rows
+// of the 64-wide K tile.  Lane l lands at row l / 8, chunk position l % 8 of
+// its group and fetches the logical chunk the row swizzle puts there, so the
+// LDS layout is the one lds_chunk_off describes.  Completion is tracked by
+// vmcnt: the wave waits for its own fetch before the workgroup barrier.
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int R, int NTL>
+struct DmaOperand {
+  static constexpr int NW = NTL / 64;
+  static constexpr int GROUPS = R / 8;
+  static constexpr int LOADS = GROUPS / NW;
+  uint32_t voff[LOADS];
+  int group0;
+  __device__ __forceinline__ void init(int ltid, int64_t ld) {
+    const int lane = ltid & 63, w = ltid >> 6;
+    group0 = w;
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int g = j * NW + w;
+      const int r = g * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ fswz(r);
+      voff[j] = (uint32_t)((r * ld + c * 8) * 2);
+    }
+  }
+  __device__ __forceinline__ void load(rsrc_t rs, __bf16* plane) const {
+#pragma unroll
+    for (int j = 0; j < LOADS; ++j) {
+      const int g = j * NW + group0;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(plane + g * 512), 16, (int)voff[j], 0, 0, 0);
+    }
+  }
+};
+
 // Buffer descriptor of the K tile starting at k0 (32-bit arithmetic only: the
 // launcher guarantees ld < 2^22, so one tile of at most 256 rows of BF16, or
 // 128 rows of FP32, spans less than 2^31 bytes).
@@ -356,6 +391,11 @@ struct FastGemm {
   typedef typename std::conditional<X3, FastOperandX3<BM, A_KMAJ, NTL>, FastOperand<BM, A_KMAJ, NTL>>::type OpA;
   typedef typename std::conditional<X3, FastOperandX3<BN, B_KMAJ, NTL>, FastOperand<BN, B_KMAJ, NTL>>::type OpB;
   static constexpr bool DO_A = ROLE != ROLE_B, DO_B = ROLE != ROLE_A;
+  // The input gradient's K-major A (dY) is fetched straight into LDS by the
+  // eight-wave kernel's A waves (no staging registers, no LDS write
+  // instructions): measured 2.7% faster for that pass, while for the forward
+  // pass (both operands K-major) register staging is 4% faster.
+  static constexpr bool DMA = !X3 && ROLE == ROLE_A && A_KMAJ && !B_KMAJ;
 
   // Accumulators hold the transposed product: acc[i][j] is the 32x32 block
   // D[n][m] = sum_k B(n,k) A(m,k), so that lane l owns output row m = l % 32
@@ -419,8 +459,13 @@ struct FastGemm {
     const int stride = gridDim.x;
     OpA opa;
     OpB opb;
-    if (DO_A) opa.init(ltid, lda);
-    if (DO_B) opb.init(ltid, ldb);
+    DmaOperand<(ROLE == ROLE_A ? BM : BN), NTL> opd;
+    if constexpr (DMA) {
+      opd.init(ltid, ROLE == ROLE_A ? lda : ldb);
+    } else {
+      if (DO_A) opa.init(ltid, lda);
+      if (DO_B) opb.init(ltid, ldb);
+    }
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -488,16 +533,33 @@ struct FastGemm {
       if (DO_A) opa.store(stage, stage + PLANE_A);
       if (DO_B) opb.store(stage + B_BASE, stage + B_BASE + PLANE_B);
     };
+    auto dma = [&](const StepCursor& L, __bf16* stage) {
+      const bool ok = cursor_valid(um, L);
+      const int kk = ok ? (L.kt0 + L.kt) * BK : p.K;
+      if constexpr (ROLE == ROLE_A)
+        opd.load(tile_rsrc<true, BM>(A + L.b * p.batch_a, lda, L.row0, ok ? p.M : L.row0 + 1, kk, p.K), stage);
+      else
+        opd.load(tile_rsrc<true, BN>(B + L.b * p.batch_b, ldb, L.col0, ok ? p.N : L.col0 + 1, kk, p.K), stage + B_BASE);
+    };
 
     StepCursor C = cursor_at<BM, BN>(um, blockIdx.x);
     if (!cursor_valid(um, C)) return;
     StepCursor L = C;
-    load(L);
-    L = cursor_next<BM, BN>(um, L, stride);
-    store(smem);
-    load(L);
-    L = cursor_next<BM, BN>(um, L, stride);
-    __syncthreads();
+    if constexpr (DMA) {
+      dma(L, smem);
+      L = cursor_next<BM, BN>(um, L, stride);
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();
+      dma(L, smem + STAGE);
+      L = cursor_next<BM, BN>(um, L, stride);
+    } else {
+      load(L);
+      L = cursor_next<BM, BN>(um, L, stride);
+      store(smem);
+      load(L);
+      L = cursor_next<BM, BN>(um, L, stride);
+      __syncthreads();
+    }
     DPG_READ_FRAGS(smem, 0, 0);
 
     constexpr int NM = FM * FN * (X3 ? 3 : 1);  // MFMAs per k-step
@@ -519,7 +581,7 @@ struct FastGemm {
       // always issue MFMAs.
       DPG_READ_FRAGS(cur, 2, 0);
       DPG_MFMAS(1, 0, FM);
-      if constexpr (ROLE != ROLE_B) {
+      if constexpr (ROLE != ROLE_B && !DMA) {
         store(nxt);
         load(L);
         sched_step<NM, NR, NW, NV>();
@@ -530,7 +592,7 @@ struct FastGemm {
       // k-step 2: fragments of step 3
       DPG_READ_FRAGS(cur, 3, 1);
       DPG_MFMAS(0, 0, FM);
-      if constexpr (ROLE == ROLE_B) {
+      if constexpr (ROLE == ROLE_B && !DMA) {
         store(nxt);
         load(L);
         sched_step<NM, NR, NW, NV>();
@@ -540,10 +602,15 @@ struct FastGemm {
       __builtin_amdgcn_sched_barrier(0);
       // k-step 3: half the MFMAs, barrier, first fragments of the next K tile, rest
       DPG_MFMAS(1, 0, FM / 2);
+      if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
+      if constexpr (DMA) dma(L, (__bf16*)cur);
       DPG_READ_FRAGS(nxt, 0, 0);  // garbage after the last step (in-bounds LDS)
       DPG_MFMAS(1, FM / 2, FM);
-      sched_step<NM / 2, NR, 0, 0>();
+      if constexpr (DMA)
+        sched_step<NM / 2, NR, 0, decltype(opd)::LOADS>();
+      else
+        sched_step<NM / 2, NR, 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
       L = cursor_next<BM, BN>(um, L, stride);
       if (C.kt + 1 >= C.nkt) {
