@@ -10,13 +10,15 @@ namespace dpg {
 
 // Rates are per CU, shared by the workgroups resident on it (measured on
 // MI355X: one 64x64 workgroup already sustains most of what a CU gives that
-// kernel).  BF16x3 plans use the pipelined 128x128 tile or the generic 64x64
-// one.
+// kernel, while the 128x128 tile gains from its second workgroup: FP32-output
+// projections at 16384 tokens ran at 0.40-0.45 of the CU rate with two per CU,
+// against 0.26-0.41 with one depending on layout).  BF16x3 plans use the
+// pipelined 128x128 tile or the generic 64x64 one.
 const TileShape kTiles[kNumTiles] = {
-    // bm, bn, bk, threads, occupancy, eff, x3_eff, x3_occupancy, x3_ok, fast_ok
-    {256, 256, 64, 256, 1, 0.55, 0.0, 0, false, true},
-    {128, 128, 64, 256, 2, 0.36, 0.28, 1, true, true},
-    {64, 64, 64, 256, 4, 0.20, 0.19, 2, true, false},
+    // bm, bn, bk, threads, occupancy, eff, eff_one, x3_eff, x3_occupancy, x3_ok, fast_ok
+    {256, 256, 64, 256, 1, 0.55, 0.0, 0.0, 0, false, true},
+    {128, 128, 64, 256, 2, 0.43, 0.36, 0.28, 1, true, true},
+    {64, 64, 64, 256, 4, 0.20, 0.0, 0.19, 2, true, false},
 };
 
 namespace {
@@ -73,7 +75,9 @@ double estimate_us(const TileShape& ts, bool fast, int64_t batch, int64_t M, int
   const double flop_unit = 2.0 * ts.bm * ts.bn * (double)(kt_per * ts.bk) * (x3 ? 3 : 1);
   const int64_t occ_used = std::min<int64_t>(x3 ? ts.x3_occupancy : ts.occupancy, cdiv(units, cus));
   const int64_t rounds = cdiv(units, (int64_t)cus * occ_used);
-  const double cu_rate = kCuFlops * (x3 ? ts.x3_eff : ts.eff);
+  // a lone four-wave workgroup leaves the CU's MFMA pipes idler than two do
+  const double eff = (occ_used == 1 && ts.eff_one > 0) ? ts.eff_one : ts.eff;
+  const double cu_rate = kCuFlops * (x3 ? ts.x3_eff : eff);
   const double epi_us = (double)occ_used * ts.bm * ts.bn * (s > 1 ? 4 : out_bytes) / kCuStore * 1e6;
   const double mfma_round_us = (double)occ_used * flop_unit / cu_rate * 1e6;
   double t_gemm = fast ? rounds * mfma_round_us + kUnitUs + epi_us : rounds * (mfma_round_us + kUnitUs + epi_us);

@@ -16,6 +16,7 @@ struct TileShape {
   int threads;
   int occupancy;   // workgroups that fit one CU at once
   double eff;      // sustained fraction of the CU's MFMA rate, BF16 operands (model)
+  double eff_one;  // the same when only one of its workgroups runs on a CU (0: as eff)
   double x3_eff;   // the same for BF16x3 (FP32 operands), counted in executed FLOP
   int x3_occupancy;  // workgroups per CU with BF16x3 (hi and lo planes)
   bool x3_ok;      // BF16x3 plans use this tile
