@@ -74,6 +74,24 @@ def clock_under_load():
         return None
     m = re.search(r"clock_ghz_under_load:\s*([0-9.]+)", open(path).read())
     return float(m.group(1)) if m else None
+
+
+def read_mfma_busy(kernel_pass):
+    """MFMA-busy fraction and engine clock of one pass's GEMM kernel from the
+    committed rocprofv3 counter summary, if it was taken from the current
+    kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, "gemm_4096x12288_T16384_mfma_busy.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_hash:\s*(\S+)", text)
+    r = re.search(r"^%s: mfma_busy ([0-9.]+) clock_ghz ([0-9.]+)" % kernel_pass, text, re.M)
+    if not m or not r or m.group(1) != kernel_source_hash():
+        return None
+    return {"mfma_busy": float(r.group(1)), "clock_ghz": float(r.group(2)),
+            "source": "rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE (profiles/)"}
+
+
 PASS_KERNEL_TAG = {  # template arguments (A K-major, B K-major) of each pass's GEMM kernel
     "fwd": "true, true", "dgrad": "true, false", "wgrad": "false, false"}
 COPY_BYTES = 1 << 30
@@ -175,6 +193,42 @@ def summarize_pmc(fetch_csv, write_csv, command):
             f.write("algorithmic bytes (operands once + output): %.4g (ratio %.2f)\n"
                     % (alg + out_b, (fetch_b + write_b) / (alg + out_b)))
         print("wrote", path)
+
+
+def summarize_busy(counter_csv, command, xcds=8, cus=256):
+    """Writes profiles/gemm_4096x12288_T16384_mfma_busy.txt from a rocprofv3
+    --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE run: per pass, the engine
+    clock (GRBM_GUI_ACTIVE counts every XCD, so cycles / XCDs / duration) and
+    the fraction of SIMD cycles the MFMA pipes were busy
+    (SQ_VALU_MFMA_BUSY_CYCLES / (cycles x CUs x 4 SIMDs))."""
+    import csv
+    disp = {}
+    for r in csv.DictReader(open(counter_csv)):
+        d = disp.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"], "t0": int(r["Start_Timestamp"]),
+                                               "t1": int(r["End_Timestamp"])})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    path = os.path.join(PROFILE_DIR, "gemm_4096x12288_T16384_mfma_busy.txt")
+    with open(path, "w") as f:
+        f.write("MFMA pipe utilisation of the 4096->12288 GEMM passes (T=16384, BF16 out), rocprofv3 PMC on MI355X\n")
+        f.write("command:\n  %s\n" % command)
+        f.write("kernel_source_hash: %s\n" % kernel_source_hash())
+        f.write("clock = GRBM_GUI_ACTIVE / %d XCDs / duration; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+                "(GRBM_GUI_ACTIVE / %d x %d CUs x 4 SIMDs)\n" % (xcds, xcds, cus))
+        for name, tag in PASS_KERNEL_TAG.items():
+            ds = [d for d in disp.values() if "gemm_fast_kernel<256, 256" in d["name"] and (", %s, 0," % tag) in d["name"]]
+            if not ds:
+                continue
+            d = ds[-1]
+            dur_ns = d["t1"] - d["t0"]
+            cyc = d["GRBM_GUI_ACTIVE"] / xcds
+            busy = d["SQ_VALU_MFMA_BUSY_CYCLES"] / (cyc * cus * 4)
+            ghz = cyc / dur_ns
+            flop = 2.0 * T_BIG * N_BIG * K_BIG
+            f.write("%s: mfma_busy %.3f clock_ghz %.3f duration_us %.1f  (raw GRBM_GUI_ACTIVE %.4g, "
+                    "SQ_VALU_MFMA_BUSY_CYCLES %.4g; %.0f TFLOP/s under the profiler = %.3f of the peak at that clock)\n"
+                    % (name, busy, ghz, dur_ns / 1e3, d["GRBM_GUI_ACTIVE"], d["SQ_VALU_MFMA_BUSY_CYCLES"],
+                       flop / dur_ns / 1e3, flop / dur_ns / 1e3 / (cus * 4096 * ghz / 1e3)))
+    print("wrote", path)
 
 
 def summarize_trace(stats_csv, command, out_name="bench_4096x12288_T16384_kernel_trace.txt"):
@@ -358,12 +412,16 @@ def main():
                     help="run the forward GEMM in a loop for SECONDS (to read the clock under load)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "COMMAND"))
+    ap.add_argument("--summarize-busy", nargs=2, metavar=("COUNTER_CSV", "COMMAND"))
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace)
+        return
+    if args.summarize_busy:
+        summarize_busy(*args.summarize_busy)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -442,6 +500,9 @@ def main():
         adj = PEAK_BF16_TFLOPS * clk / 2.4
         roofline["clock_adjusted"] = {"clock_ghz": clk, "peak": round(adj, 1), "frac": round(achieved / adj, 4),
                                       "source": "rocm-smi sclk under sustained forward-GEMM load (profiles/)"}
+    busy = read_mfma_busy(dominant)
+    if busy:
+        roofline["counters"] = busy
 
     skinny = []
     if not args.skip_skinny:
