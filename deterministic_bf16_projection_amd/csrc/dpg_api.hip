@@ -102,14 +102,17 @@ struct SkinnyRow {
 };
 
 SkinnyFn lookup_skinny_kernel(int nb, int cb, int out_kind) {
-  static const SkinnyFn table[2][2][3] = {
+  // column blocks 1, 2 or 4 (4 only with two row blocks)
+  static const SkinnyFn table[2][3][3] = {
       {{SkinnyRow<1, 1>::fns[0], SkinnyRow<1, 1>::fns[1], SkinnyRow<1, 1>::fns[2]},
-       {SkinnyRow<1, 2>::fns[0], SkinnyRow<1, 2>::fns[1], SkinnyRow<1, 2>::fns[2]}},
+       {SkinnyRow<1, 2>::fns[0], SkinnyRow<1, 2>::fns[1], SkinnyRow<1, 2>::fns[2]},
+       {nullptr, nullptr, nullptr}},
       {{SkinnyRow<2, 1>::fns[0], SkinnyRow<2, 1>::fns[1], SkinnyRow<2, 1>::fns[2]},
-       {SkinnyRow<2, 2>::fns[0], SkinnyRow<2, 2>::fns[1], SkinnyRow<2, 2>::fns[2]}},
+       {SkinnyRow<2, 2>::fns[0], SkinnyRow<2, 2>::fns[1], SkinnyRow<2, 2>::fns[2]},
+       {SkinnyRow<2, 4>::fns[0], SkinnyRow<2, 4>::fns[1], SkinnyRow<2, 4>::fns[2]}},
   };
-  if (nb < 1 || nb > 2 || cb < 1 || cb > 2 || out_kind < 0 || out_kind > 2) return nullptr;
-  return table[nb - 1][cb - 1][out_kind];
+  if (nb < 1 || nb > 2 || (cb != 1 && cb != 2 && cb != 4) || out_kind < 0 || out_kind > 2) return nullptr;
+  return table[nb - 1][cb == 4 ? 2 : cb - 1][out_kind];
 }
 
 int tile_threads(int tile) { return kTiles[tile].threads; }

@@ -5,8 +5,9 @@
 // Work unit = (all N rows, a block of CB * 64 columns of K, token split).  A
 // workgroup has 8 waves arranged as NB row blocks x CB column blocks x TG token
 // groups (NB * CB * TG = 8; NB = 1 for N <= 64, 2 for N <= 128; CB = 2, or 1
-// when a small forced split count leaves too few units), each wave owning a
-// 64 x 64 block of dW.  Per iteration, token group g takes the unit's 64-token
+// when a small forced split count leaves too few units, or 4 with two row
+// blocks over long token ranges, where each dY tile then serves 256 columns),
+// each wave owning a 64 x 64 block of dW.  Per iteration, token group g takes the unit's 64-token
 // block (iteration * TG + g): its X tiles (64 tokens x 64 columns) and dY tiles
 // (64 tokens x 64 rows) are fetched once with 16-byte buffer loads (rows past T
 // read as zero), transposed in registers (8x8 BF16 blocks) and written
@@ -36,7 +37,7 @@ template <int NB, int CB, int OUT>
 __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
   constexpr int W = 8;
   constexpr int TG = W / (NB * CB);     // token groups
-  static_assert((NB == 1 || NB == 2) && (CB == 1 || CB == 2), "row and column blocks");
+  static_assert((NB == 1 || NB == 2) && (CB == 1 || CB == 2 || (CB == 4 && NB == 2)), "row and column blocks");
   constexpr int TILE = 4096;            // BF16 elements of one transposed 64x64 tile
   constexpr int X_TILES = CB * TG, Y_TILES = NB * TG;
   constexpr int RED_LD = 68;            // FP32 row stride of the reduction buffer

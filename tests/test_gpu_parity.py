@@ -269,14 +269,16 @@ def test_skinny_wgrad(skinny_x, T, K, N):
 
 
 # Exact-integer inputs through the skinny kernel: one and two 64-row blocks of
-# dW, 64- and 128-column units (auto plans use 128 columns when enough units
-# exist; forced small split counts use 64), ragged token tails.
+# dW, 64-, 128- and 256-column units (auto plans use 128 columns when enough
+# units exist, 256 for two row blocks over long token ranges; forced small
+# split counts use 64), ragged token tails.
 # (The planner's choices for these shapes are checked on the CPU.)
 SKINNY_EXACT = [
     (4031, 128, 4096),   # two row blocks; 63 token blocks, last holds 63
     (16384, 48, 5120),   # one row block, ragged N inside the block
     (1025, 104, 1024),   # two row blocks, N ragged; 17 token blocks, last holds 1
     (16384, 128, 4096),  # two row blocks, 128-column units
+    (65537, 104, 3968),  # two row blocks, N ragged, 256-column units, last unit half outside K
 ]
 
 

@@ -72,8 +72,9 @@ def test_forced_split_one():
 def test_skinny_unit_shapes():
     """Skinny weight gradients: 128-column units when they give at least half
     as many workgroups as CUs, 64-column units otherwise (forced small split
-    counts); one or two 64-row blocks of dW.  The exact-integer GPU shapes
-    together reach all four kernel variants."""
+    counts), 256-column units for two row blocks over long token ranges; one or
+    two 64-row blocks of dW.  The exact-integer GPU shapes together reach all
+    five kernel variants."""
     def tile(T, N, K, det, split):
         p = plan(2, T, N, K, out=F32, det=det, split=split)
         assert p["kernel"] == "skinny", p
@@ -83,11 +84,18 @@ def test_skinny_unit_shapes():
     assert tile(16384, 64, 4096, 0, 2) == "64x64x64"
     assert tile(16384, 128, 4096, 0, 1) == "128x64x64"
     assert tile(16384, 48, 5120, 1, 0) == "64x128x64"
+    # 256-column units: two row blocks, at least 2048 tokens per split, a unit per CU
+    assert tile(65537, 128, 4096, 1, 0) == "128x256x64"
+    assert tile(65537, 64, 4096, 1, 0) == "64x128x64"
+    assert tile(65537, 128, 4096, 0, 2) == "128x64x64"
+    assert tile(16384, 128, 4096, 1, 0) == "128x128x64"
+    assert tile(32768, 104, 4096, 1, 0) == "128x256x64"
+    assert tile(32640, 104, 4096, 1, 0) == "128x128x64"
     seen = set()
-    for T, N, K in [(4031, 128, 4096), (16384, 48, 5120), (1025, 104, 1024), (16384, 128, 4096)]:
+    for T, N, K in [(4031, 128, 4096), (16384, 48, 5120), (1025, 104, 1024), (16384, 128, 4096), (65537, 104, 3968)]:
         for det, split in [(1, 0), (0, 1), (0, 2), (1, 3)]:
             seen.add(tile(T, N, K, det, split))
-    assert seen == {"64x64x64", "64x128x64", "128x64x64", "128x128x64"}
+    assert seen == {"64x64x64", "64x128x64", "128x64x64", "128x128x64", "128x256x64"}
 
 
 def test_router_uses_bf16x3():
