@@ -22,7 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libdpg.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "dpg.h")
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError("libdpg.so is not built; run `python -m deterministic_bf16_projection_amd.build` "
+    raise ImportError("libdpg.so is not built; run `python deterministic_bf16_projection_amd/build.py` "
                       "(or __graft_entry__.build()) first")
 
 _lib = ctypes.CDLL(LIB_PATH)

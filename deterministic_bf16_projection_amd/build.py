@@ -1,8 +1,9 @@
 """Builds libdpg.so, the library's gfx950 shared object, in this directory.
 
 hipcc compiles the HIP kernels ahead of time for gfx950 (no JIT) together with
-the host planner and the C ABI.  Usage: ``python -m
-deterministic_bf16_projection_amd.build`` or ``build()``.
+the host planner and the C ABI.  Usage: ``python
+deterministic_bf16_projection_amd/build.py`` (run as a file: importing the
+package needs the library) or ``build()`` of this module loaded by path.
 """
 import os
 import shutil
