@@ -35,7 +35,8 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz (dense)
 PEAK_HBM_GBPS = 8000.0
 T_BIG, N_BIG, K_BIG = 16384, 12288, 4096
 SKINNY = [(4096, 64), (4096, 128), (5120, 48), (5120, 64)]
-T_SKINNY = 16384
+# token counts timed: all modes at 16384, the planner's plan also at 65537
+SKINNY_RUNS = [(16384, [(True, 0), (False, 1), (False, 2)]), (65537, [(True, 0)])]
 KERNEL_SOURCES = ["deterministic_bf16_projection_amd/csrc/gemm_fast.h",
                   "deterministic_bf16_projection_amd/csrc/gemm_kernel.h",
                   "deterministic_bf16_projection_amd/csrc/device_common.h"]
@@ -508,31 +509,32 @@ def main():
     if not args.skip_skinny:
         del Y, DX, DW
         torch.cuda.empty_cache()
-        for K, N in SKINNY:
-            xs = to_dev(dpg_inputs.normal_bf16((T_SKINNY, K), 1.0, 0, 0))
-            dys = to_dev(dpg_inputs.normal_bf16((T_SKINNY, N), 1.0, 0, 2))
-            out = torch.empty((N, K), dtype=torch.float32, device=dev)
-            for det, split in [(True, 0), (False, 1), (False, 2)]:
-                ws_n = dpg.workspace_size(dpg.PASS_WGRAD, T_SKINNY, N, K, torch.float32, det, split)
-                ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
-                for _ in range(5):
-                    dpg.dpg_wgrad(dys, xs, out=out, deterministic=det, split_k=split, workspace=ws)
-                reps = 50
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for _ in range(reps):
-                    dpg.dpg_wgrad(dys, xs, out=out, deterministic=det, split_k=split, workspace=ws)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) * 1e3 / reps
-                nbytes = 2.0 * T_SKINNY * K + 2.0 * T_SKINNY * N + 4.0 * N * K
-                skinny.append({"shape": "%d->%d" % (K, N), "T": T_SKINNY, "out": "f32",
-                               "mode": "deterministic, planner splits" if det else "split_k=%d" % split,
-                               "us": round(us, 2),
-                               "GBps": round(nbytes / us / 1e3, 1),
-                               "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 4),
-                               "plan": dpg.plan_describe(dpg.PASS_WGRAD, T_SKINNY, N, K, torch.float32, det, split)})
-            del xs, dys, out
+        for T_S, modes in SKINNY_RUNS:
+            for K, N in SKINNY:
+                xs = to_dev(dpg_inputs.normal_bf16((T_S, K), 1.0, 0, 0))
+                dys = to_dev(dpg_inputs.normal_bf16((T_S, N), 1.0, 0, 2))
+                out = torch.empty((N, K), dtype=torch.float32, device=dev)
+                for det, split in modes:
+                    ws_n = dpg.workspace_size(dpg.PASS_WGRAD, T_S, N, K, torch.float32, det, split)
+                    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
+                    for _ in range(5):
+                        dpg.dpg_wgrad(dys, xs, out=out, deterministic=det, split_k=split, workspace=ws)
+                    reps = 50 if T_S <= 16384 else 20
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    for _ in range(reps):
+                        dpg.dpg_wgrad(dys, xs, out=out, deterministic=det, split_k=split, workspace=ws)
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    us = e0.elapsed_time(e1) * 1e3 / reps
+                    nbytes = 2.0 * T_S * K + 2.0 * T_S * N + 4.0 * N * K
+                    skinny.append({"shape": "%d->%d" % (K, N), "T": T_S, "out": "f32",
+                                   "mode": "deterministic, planner splits" if det else "split_k=%d" % split,
+                                   "us": round(us, 2),
+                                   "GBps": round(nbytes / us / 1e3, 1),
+                                   "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 4),
+                                   "plan": dpg.plan_describe(dpg.PASS_WGRAD, T_S, N, K, torch.float32, det, split)})
+                del xs, dys, out
 
     secondary = None if args.skip_secondary else secondary_configs(dpg, dpg_inputs, torch, to_dev)
 
