@@ -98,6 +98,22 @@ def test_skinny_unit_shapes():
     assert seen == {"64x64x64", "64x128x64", "128x64x64", "128x128x64", "128x256x64"}
 
 
+def test_medium_projection_plans():
+    """Plans the cost model picks for the checkpointed-step shapes (measured on
+    MI355X to be the fastest or within 3% of it among forced split counts):
+    4096->1024 passes whole-K on 256x256 tiles except the weight gradient
+    (4 splits); 4096->512 forward on two 128x128 workgroups per CU, unsplit."""
+    def pick(pass_, N):
+        p = plan(pass_, 16384, N, 4096, out=F32)
+        return p["tile"], p["splits"]
+    assert pick(0, 1024) == ("256x256x64", "1")
+    assert pick(1, 1024) == ("256x256x64", "1")
+    assert pick(2, 1024) == ("256x256x64", "4")
+    assert pick(0, 512) == ("128x128x64", "1")
+    assert pick(1, 512) == ("256x256x64", "1")
+    assert pick(2, 512) == ("256x256x64", "8")
+
+
 def test_router_uses_bf16x3():
     p = plan(3, 64, 256, 4096, out=F32)
     assert p["x3"] == "1"
