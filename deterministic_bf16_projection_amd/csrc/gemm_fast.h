@@ -635,6 +635,9 @@ struct FastGemm {
       __builtin_amdgcn_sched_barrier(0);
       // k-step 3: half the MFMAs, barrier, first fragments of the next K tile, rest
       DPG_MFMAS(1, 0, FM / 2);
+      // keep these MFMAs ahead of the barrier: MFMAs have no side effects, so
+      // the scheduler would otherwise sink them past it
+      __builtin_amdgcn_sched_barrier(0);
       if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
       if constexpr (DMA) dma(L, (__bf16*)cur);
