@@ -525,19 +525,31 @@ struct FastGemm {
 
     bf16x8 fa[2][FM], fb[2][FN];
     bf16x8 fal[2][FM], fbl[2][FN];  // BF16x3 lo fragments
+#define DPG_READ_A(stage, S, BUF, i)                                                                         \
+  do {                                                                                                     \
+    fa[BUF][i] = as_bf16x8(*(const u32x4*)((stage) + a_row[i] + koff[(S) ^ (2 * ((i) & 1))]));             \
+    if constexpr (X3)                                                                                      \
+      fal[BUF][i] = as_bf16x8(*(const u32x4*)((stage) + PLANE_A + a_row[i] + koff[(S) ^ (2 * ((i) & 1))])); \
+  } while (0)
+#define DPG_READ_B(stage, S, BUF, j)                                                                         \
+  do {                                                                                                     \
+    fb[BUF][j] = as_bf16x8(*(const u32x4*)((stage) + b_row[j] + koff[(S) ^ (2 * ((j) & 1))]));             \
+    if constexpr (X3)                                                                                      \
+      fbl[BUF][j] = as_bf16x8(*(const u32x4*)((stage) + PLANE_B + b_row[j] + koff[(S) ^ (2 * ((j) & 1))])); \
+  } while (0)
     // fragments of k-step S (0..3) of a stage into buffer BUF (hi and, for
-    // BF16x3, lo planes)
+    // BF16x3, lo planes).  Weight gradient: in the order the MFMAs use them
+    // (A row 0, all of B, the other A rows), measured 2.5% faster there; the
+    // other layouts keep A before B, which measured 1.4% faster for the forward.
 #define DPG_READ_FRAGS(stage, S, BUF)                                                                      \
   do {                                                                                                     \
-    _Pragma("unroll") for (int i = 0; i < FM; ++i) {                                                       \
-      fa[BUF][i] = as_bf16x8(*(const u32x4*)((stage) + a_row[i] + koff[(S) ^ (2 * (i & 1))]));             \
-      if constexpr (X3)                                                                                    \
-        fal[BUF][i] = as_bf16x8(*(const u32x4*)((stage) + PLANE_A + a_row[i] + koff[(S) ^ (2 * (i & 1))])); \
-    }                                                                                                      \
-    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                                       \
-      fb[BUF][j] = as_bf16x8(*(const u32x4*)((stage) + b_row[j] + koff[(S) ^ (2 * (j & 1))]));             \
-      if constexpr (X3)                                                                                    \
-        fbl[BUF][j] = as_bf16x8(*(const u32x4*)((stage) + PLANE_B + b_row[j] + koff[(S) ^ (2 * (j & 1))])); \
+    if constexpr (!A_KMAJ) {                                                                               \
+      DPG_READ_A(stage, S, BUF, 0);                                                                        \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) DPG_READ_B(stage, S, BUF, j);                         \
+      _Pragma("unroll") for (int i = 1; i < FM; ++i) DPG_READ_A(stage, S, BUF, i);                         \
+    } else {                                                                                               \
+      _Pragma("unroll") for (int i = 0; i < FM; ++i) DPG_READ_A(stage, S, BUF, i);                         \
+      _Pragma("unroll") for (int j = 0; j < FN; ++j) DPG_READ_B(stage, S, BUF, j);                         \
     }                                                                                                      \
   } while (0)
     // MFMAs of rows [I0, I1) of the wave tile from fragment buffer BUF; BF16x3
@@ -662,6 +674,8 @@ struct FastGemm {
       C = cursor_next<BM, BN>(um, C, stride);
     }
 #undef DPG_READ_FRAGS
+#undef DPG_READ_A
+#undef DPG_READ_B
 #undef DPG_MFMAS
   }
 };
