@@ -154,6 +154,7 @@ def _workspace(pass_, T, N, K, out_code, det, split_k, workspace, device):
         raise DpgError(1, "dpg_workspace_size")
     if need == 0:
         return None, 0
+    _check_workspace(workspace, device)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
     if workspace.numel() * workspace.element_size() < need:
@@ -182,6 +183,30 @@ def _check_in(t, dtype, name):
         raise ValueError("%s must be a device tensor" % name)
 
 
+def _check_same_device(*named):
+    """Every (name, tensor) pair on the first one's device."""
+    dev = named[0][1].device
+    for name, t in named[1:]:
+        if t.device != dev:
+            raise ValueError("%s is on %s, expected %s" % (name, t.device, dev))
+
+
+def _check_out(out, shape, device, name="out"):
+    """A caller-supplied output must be a device tensor of exactly the output's
+    shape (the kernels write every element of it)."""
+    if not out.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if out.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, out.device, device))
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(out.shape)))
+
+
+def _check_workspace(workspace, device):
+    if workspace is not None and (not workspace.is_cuda or workspace.device != device):
+        raise ValueError("workspace must be a device tensor on %s" % device)
+
+
 def dpg_forward(x, w, out=None, out_dtype=torch.bfloat16, deterministic=True, split_k=0, workspace=None,
                 stream=None):
     """Y[T,N] = X[T,K] W[N,K]^T (BF16 operands, FP32 accumulation)."""
@@ -191,8 +216,10 @@ def dpg_forward(x, w, out=None, out_dtype=torch.bfloat16, deterministic=True, sp
     N = w.shape[0]
     if w.shape[1] != K:
         raise ValueError("w must be [N, K]")
+    _check_same_device(("x", x), ("w", w))
     if out is None:
         out = torch.empty((T, N), dtype=out_dtype, device=x.device)
+    _check_out(out, (T, N), x.device)
     return _call("dpg_forward", PASS_FORWARD, x, w, out, _code(out.dtype), T, N, K, deterministic, split_k,
                  workspace, stream)
 
@@ -206,8 +233,10 @@ def dpg_dgrad(dy, w, out=None, out_dtype=torch.bfloat16, deterministic=True, spl
     K = w.shape[1]
     if w.shape[0] != N:
         raise ValueError("w must be [N, K]")
+    _check_same_device(("dy", dy), ("w", w))
     if out is None:
         out = torch.empty((T, K), dtype=out_dtype, device=dy.device)
+    _check_out(out, (T, K), dy.device)
     return _call("dpg_dgrad", PASS_DGRAD, dy, w, out, _code(out.dtype), T, N, K, deterministic, split_k,
                  workspace, stream)
 
@@ -221,8 +250,10 @@ def dpg_wgrad(dy, x, out=None, out_dtype=torch.bfloat16, deterministic=True, spl
     K = x.shape[1]
     if x.shape[0] != T:
         raise ValueError("x must be [T, K]")
+    _check_same_device(("dy", dy), ("x", x))
     if out is None:
         out = torch.empty((N, K), dtype=out_dtype, device=dy.device)
+    _check_out(out, (N, K), dy.device)
     return _call("dpg_wgrad", PASS_WGRAD, dy, x, out, _code(out.dtype), T, N, K, deterministic, split_k,
                  workspace, stream)
 
@@ -233,8 +264,13 @@ def dpg_router_forward(x, w, out=None, deterministic=True, split_k=0, workspace=
     _check_in(w, torch.float32, "w")
     T, H = x.shape
     E = w.shape[0]
+    if w.shape[1] != H:
+        raise ValueError("w must be [E, H]")
+    _check_same_device(("x", x), ("w", w))
     if out is None:
         out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check_in(out, torch.float32, "out")
+    _check_out(out, (T, E), x.device)
     return _call("dpg_router_forward", PASS_ROUTER_FORWARD, x, w, out, F32, T, E, H, deterministic, split_k,
                  workspace, stream)
 
@@ -245,8 +281,13 @@ def dpg_router_dgrad(dy, w, out=None, deterministic=True, split_k=0, workspace=N
     _check_in(w, torch.float32, "w")
     T, E = dy.shape
     H = w.shape[1]
+    if w.shape[0] != E:
+        raise ValueError("w must be [E, H]")
+    _check_same_device(("dy", dy), ("w", w))
     if out is None:
         out = torch.empty((T, H), dtype=torch.float32, device=dy.device)
+    _check_in(out, torch.float32, "out")
+    _check_out(out, (T, H), dy.device)
     return _call("dpg_router_dgrad", PASS_ROUTER_DGRAD, dy, w, out, F32, T, E, H, deterministic, split_k,
                  workspace, stream)
 
@@ -257,8 +298,13 @@ def dpg_router_wgrad(dy, x, out=None, deterministic=True, split_k=0, workspace=N
     _check_in(x, torch.float32, "x")
     T, E = dy.shape
     H = x.shape[1]
+    if x.shape[0] != T:
+        raise ValueError("x must be [T, H]")
+    _check_same_device(("dy", dy), ("x", x))
     if out is None:
         out = torch.empty((E, H), dtype=torch.float32, device=dy.device)
+    _check_in(out, torch.float32, "out")
+    _check_out(out, (E, H), dy.device)
     return _call("dpg_router_wgrad", PASS_ROUTER_WGRAD, dy, x, out, F32, T, E, H, deterministic, split_k,
                  workspace, stream)
 
@@ -316,6 +362,7 @@ def _batched_ws(pass_, wl, batch, T, N, K, out_code, det, split_k, workspace, de
         raise DpgError(1, "dpg_workspace_size_batched")
     if need == 0:
         return None, 0
+    _check_workspace(workspace, device)
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
     if workspace.numel() * workspace.element_size() < need:
@@ -336,8 +383,10 @@ def dpg_forward_batched(x, w, out=None, out_dtype=torch.bfloat16, weight_layout=
     N = w.shape[-2] if wl == 0 else w.shape[-1]
     if (w.shape[-1] if wl == 0 else w.shape[-2]) != K:
         raise ValueError("weight does not match K")
+    _check_same_device(("x", x), ("w", w))
     if out is None:
         out = torch.empty((batch, T, N), dtype=out_dtype, device=x.device)
+    _check_out(out, (batch, T, N), x.device)
     x3, sx, ldx = _batched(x, "x", batch)
     w3, sw, ldw = _batched(w, "w", batch)
     o3, so, ldo = _batched(out, "out", batch)
@@ -362,8 +411,10 @@ def dpg_dgrad_batched(dy, w, out=None, out_dtype=torch.bfloat16, weight_layout="
     K = w.shape[-1] if wl == 0 else w.shape[-2]
     if (w.shape[-2] if wl == 0 else w.shape[-1]) != N:
         raise ValueError("weight does not match N")
+    _check_same_device(("dy", dy), ("w", w))
     if out is None:
         out = torch.empty((batch, T, K), dtype=out_dtype, device=dy.device)
+    _check_out(out, (batch, T, K), dy.device)
     d3, sd, ldd = _batched(dy, "dy", batch)
     w3, sw, ldw = _batched(w, "w", batch)
     o3, so, ldo = _batched(out, "out", batch)
@@ -388,8 +439,11 @@ def dpg_wgrad_batched(dy, x, out=None, out_dtype=torch.bfloat16, weight_layout="
     K = x.shape[-1]
     if x.shape[-2] != T:
         raise ValueError("x must be [B, T, K]")
+    _check_same_device(("dy", dy), ("x", x))
+    oshape = (batch, N, K) if wl == 0 else (batch, K, N)
     if out is None:
-        out = torch.empty((batch, N, K) if wl == 0 else (batch, K, N), dtype=out_dtype, device=dy.device)
+        out = torch.empty(oshape, dtype=out_dtype, device=dy.device)
+    _check_out(out, oshape, dy.device)
     d3, sd, ldd = _batched(dy, "dy", batch)
     x3, sx, ldx = _batched(x, "x", batch)
     o3, so, ldo = _batched(out, "out", batch)

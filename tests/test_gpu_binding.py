@@ -1,0 +1,63 @@
+"""Argument checks of the Python binding (GPU tensors, but every case is
+rejected before any launch): outputs of the wrong shape or device, operands
+that do not match, a workspace that is not on the device."""
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+dpg = pytest.importorskip("deterministic_bf16_projection_amd")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+
+def _bf16(*shape):
+    return torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+
+
+def _f32(*shape):
+    return torch.zeros(shape, dtype=torch.float32, device="cuda")
+
+
+def test_output_shape_and_device_checked():
+    x, w, dy = _bf16(64, 128), _bf16(256, 128), _bf16(64, 256)
+    with pytest.raises(ValueError):
+        dpg.dpg_forward(x, w, out=_bf16(32, 256))          # too few rows
+    with pytest.raises(ValueError):
+        dpg.dpg_forward(x, w, out=_bf16(64, 255 + 1)[:, :248])  # too few columns
+    with pytest.raises(ValueError):
+        dpg.dpg_dgrad(dy, w, out=torch.zeros(64, 128, dtype=torch.bfloat16))  # host tensor
+    with pytest.raises(ValueError):
+        dpg.dpg_wgrad(dy, x, out=_f32(128, 256))            # transposed shape
+    with pytest.raises(TypeError):
+        dpg.dpg_forward(x, w, out=torch.zeros(64, 256, dtype=torch.float16, device="cuda"))
+    torch.cuda.synchronize()
+
+
+def test_router_operand_shapes_checked():
+    x, w, dy = _f32(64, 512), _f32(256, 512), _f32(64, 256)
+    with pytest.raises(ValueError):
+        dpg.dpg_router_forward(x, _f32(256, 520))           # H mismatch
+    with pytest.raises(ValueError):
+        dpg.dpg_router_dgrad(dy, _f32(128, 512))            # E mismatch
+    with pytest.raises(ValueError):
+        dpg.dpg_router_wgrad(dy, _f32(32, 512))             # T mismatch
+    with pytest.raises(ValueError):
+        dpg.dpg_router_forward(x, w, out=_f32(64, 128))
+    with pytest.raises(TypeError):
+        dpg.dpg_router_forward(x, w, out=_bf16(64, 256))
+
+
+def test_batched_output_shape_checked():
+    x, w = _bf16(2, 64, 128), _bf16(2, 256, 128)
+    with pytest.raises(ValueError):
+        dpg.dpg_forward_batched(x, w, out=_bf16(2, 64, 128))
+    with pytest.raises(ValueError):
+        dpg.dpg_wgrad_batched(_bf16(2, 64, 256), x, out=_bf16(2, 256, 128), weight_layout="kn")
+
+
+def test_workspace_device_checked():
+    dy, x = _bf16(4096, 64), _bf16(4096, 512)
+    host_ws = torch.zeros(1 << 20, dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        dpg.dpg_wgrad(dy, x, out_dtype=torch.float32, deterministic=False, split_k=2, workspace=host_ws)
