@@ -272,13 +272,15 @@ def cpu_baseline(target_s=20.0):
     import dpg_inputs
     import oracle
     # the first rows of the seeded X[16384, 4096] draw (numpy fills row-major)
-    x = dpg_inputs.normal_bf16((1024, K_BIG), 1.0, 0, 0)
+    max_rows = 4096
+    x = dpg_inputs.normal_bf16((max_rows, K_BIG), 1.0, 0, 0)
     w = dpg_inputs.normal_bf16((N_BIG, K_BIG), dpg_inputs.SIGMA_W, 0, 1)
     oracle.forward(x[:1], w)
+    # calibrate on 64 rows (enough to keep every host thread busy)
     t0 = time.perf_counter()
-    oracle.forward(x[:8], w)
+    oracle.forward(x[:64], w)
     dt = time.perf_counter() - t0
-    rows = int(max(8, min(1024, target_s / max(dt / 8, 1e-6))))
+    rows = int(max(64, min(max_rows, target_s / max(dt / 64, 1e-6))))
     t0 = time.perf_counter()
     oracle.forward(x[:rows], w)
     dt = time.perf_counter() - t0
