@@ -13,6 +13,7 @@
 #include "gemm_fast.h"
 #include "gemm_kernel.h"
 #include "skinny_wgrad.h"
+#include "skinny_direct.h"
 #include "planner.h"
 
 namespace dpg {
@@ -102,10 +103,16 @@ struct SkinnyRow {
 };
 
 SkinnyFn lookup_skinny_kernel(int nb, int cb, int out_kind) {
-  // column blocks 1, 2 or 4 (4 only with two row blocks)
+  // one row block and 128-column units: the kernel without LDS staging
+  if (nb == 1 && cb == 2) {
+    static const SkinnyFn direct[3] = {&skinny_direct_kernel<OUT_BF16>, &skinny_direct_kernel<OUT_F32>,
+                                       &skinny_direct_kernel<OUT_PARTIAL>};
+    return out_kind >= 0 && out_kind <= 2 ? direct[out_kind] : nullptr;
+  }
+  // LDS-staged kernel: column blocks 1, 2 or 4 (one row block: 1 only)
   static const SkinnyFn table[2][3][3] = {
       {{SkinnyRow<1, 1>::fns[0], SkinnyRow<1, 1>::fns[1], SkinnyRow<1, 1>::fns[2]},
-       {SkinnyRow<1, 2>::fns[0], SkinnyRow<1, 2>::fns[1], SkinnyRow<1, 2>::fns[2]},
+       {nullptr, nullptr, nullptr},
        {nullptr, nullptr, nullptr}},
       {{SkinnyRow<2, 1>::fns[0], SkinnyRow<2, 1>::fns[1], SkinnyRow<2, 1>::fns[2]},
        {SkinnyRow<2, 2>::fns[0], SkinnyRow<2, 2>::fns[1], SkinnyRow<2, 2>::fns[2]},

@@ -6,7 +6,8 @@
 // workgroup has 8 waves arranged as NB row blocks x CB column blocks x TG token
 // groups (NB * CB * TG = 8; NB = 1 for N <= 64, 2 for N <= 128; CB = 2, or 1
 // when a small forced split count leaves too few units, or 4 with two row
-// blocks over long token ranges, where each dY tile then serves 256 columns),
+// blocks over long token ranges, where each dY tile then serves 256 columns;
+// one row block with 128-column units runs skinny_direct.h instead),
 // each wave owning a 64 x 64 block of dW.  Per iteration, token group g takes the unit's 64-token
 // block (iteration * TG + g): its X tiles (64 tokens x 64 columns) and dY tiles
 // (64 tokens x 64 rows) are fetched once with 16-byte buffer loads (rows past T

@@ -268,10 +268,11 @@ def test_skinny_wgrad(skinny_x, T, K, N):
             assert torch.equal(again.view(torch.int16), out.view(torch.int16))
 
 
-# Exact-integer inputs through the skinny kernel: one and two 64-row blocks of
+# Exact-integer inputs through the skinny kernels: one and two 64-row blocks of
 # dW, 64-, 128- and 256-column units (auto plans use 128 columns when enough
 # units exist, 256 for two row blocks over long token ranges; forced small
-# split counts use 64), ragged token tails.
+# split counts use 64), ragged token tails.  One row block with 128-column
+# units runs the kernel without LDS staging (16384x48x5120, 16400x40x1000).
 # (The planner's choices for these shapes are checked on the CPU.)
 SKINNY_EXACT = [
     (4031, 128, 4096),   # two row blocks; 63 token blocks, last holds 63
@@ -279,6 +280,8 @@ SKINNY_EXACT = [
     (1025, 104, 1024),   # two row blocks, N ragged; 17 token blocks, last holds 1
     (16384, 128, 4096),  # two row blocks, 128-column units
     (65537, 104, 3968),  # two row blocks, N ragged, 256-column units, last unit half outside K
+    (16400, 40, 1000),   # one row block, N ragged, last 128-column unit partial, 16 splits of
+                         # 17 or 2 token blocks (one 16-token step per wave), last block 16 tokens
 ]
 
 

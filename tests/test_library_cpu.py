@@ -73,8 +73,9 @@ def test_skinny_unit_shapes():
     """Skinny weight gradients: 128-column units when they give at least half
     as many workgroups as CUs, 64-column units otherwise (forced small split
     counts), 256-column units for two row blocks over long token ranges; one or
-    two 64-row blocks of dW.  The exact-integer GPU shapes together reach all
-    five kernel variants."""
+    two 64-row blocks of dW (one row block with 128-column units runs the
+    kernel without LDS staging).  The exact-integer GPU shapes together reach
+    all six kernel variants."""
     def tile(T, N, K, det, split):
         p = plan(2, T, N, K, out=F32, det=det, split=split)
         assert p["kernel"] == "skinny", p
@@ -91,8 +92,11 @@ def test_skinny_unit_shapes():
     assert tile(16384, 128, 4096, 1, 0) == "128x128x64"
     assert tile(32768, 104, 4096, 1, 0) == "128x256x64"
     assert tile(32640, 104, 4096, 1, 0) == "128x128x64"
+    p = plan(2, 16400, 40, 1000, out=F32, det=1, split=0)
+    assert p["tile"] == "64x128x64" and p["splits"] == "16" and p["kt_per_split"] == "17", p
     seen = set()
-    for T, N, K in [(4031, 128, 4096), (16384, 48, 5120), (1025, 104, 1024), (16384, 128, 4096), (65537, 104, 3968)]:
+    for T, N, K in [(4031, 128, 4096), (16384, 48, 5120), (1025, 104, 1024), (16384, 128, 4096), (65537, 104, 3968),
+                    (16400, 40, 1000)]:
         for det, split in [(1, 0), (0, 1), (0, 2), (1, 3)]:
             seen.add(tile(T, N, K, det, split))
     assert seen == {"64x64x64", "64x128x64", "128x64x64", "128x128x64", "128x256x64"}
