@@ -37,14 +37,22 @@ T_BIG, N_BIG, K_BIG = 16384, 12288, 4096
 SKINNY = [(4096, 64), (4096, 128), (5120, 48), (5120, 64)]
 # token counts timed: all modes at 16384, the planner's plan also at 65537
 SKINNY_RUNS = [(16384, [(True, 0), (False, 1), (False, 2)]), (65537, [(True, 0)])]
+SKINNY_T = 16384
+SKINNY_SOURCES = ["deterministic_bf16_projection_amd/csrc/skinny_wgrad.h",
+                  "deterministic_bf16_projection_amd/csrc/skinny_direct.h",
+                  "deterministic_bf16_projection_amd/csrc/gemm_kernel.h"]
 KERNEL_SOURCES = ["deterministic_bf16_projection_amd/csrc/gemm_fast.h",
                   "deterministic_bf16_projection_amd/csrc/gemm_kernel.h",
                   "deterministic_bf16_projection_amd/csrc/device_common.h"]
 
 
-def kernel_source_hash():
+def skinny_source_hash():
+    return kernel_source_hash(SKINNY_SOURCES)
+
+
+def kernel_source_hash(sources=None):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -121,6 +129,77 @@ def profile_run():
     DW = dpg.dpg_wgrad(DY, X)
     torch.cuda.synchronize()
     print("profile run done", Y.shape, DX.shape, DW.shape)
+
+
+def profile_skinny():
+    """The skinny weight gradients once each (T=16384, FP32 out, planner
+    splits) after a plain 1 GiB device copy (counter calibration)."""
+    import numpy as np
+    import torch
+    import dpg_inputs
+    import deterministic_bf16_projection_amd as dpg
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    for K, N in SKINNY:
+        xs = to_dev(dpg_inputs.normal_bf16((SKINNY_T, K), 1.0, 0, 0))
+        dys = to_dev(dpg_inputs.normal_bf16((SKINNY_T, N), 1.0, 0, 2))
+        out = dpg.dpg_wgrad(dys, xs, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        print("skinny %d->%d done" % (K, N), tuple(out.shape), flush=True)
+
+
+def summarize_skinny_pmc(fetch_csv, write_csv, command):
+    """Writes profiles/skinny_wgrad_T16384_f32_pmc.txt from two rocprofv3 --pmc
+    runs of --profile-skinny (FETCH_SIZE, WRITE_SIZE): HBM bytes of each skinny
+    weight gradient (main kernel + split reduction) against its algorithmic
+    bytes."""
+    import csv
+
+    def per_dispatch(path):
+        d = {}
+        for r in csv.DictReader(open(path)):
+            e = d.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])
+            e[1] += float(r["Counter_Value"])
+        return [d[k] for k in sorted(d)]
+    fetch, write = per_dispatch(fetch_csv), per_dispatch(write_csv)
+    copy_f = max(v for k, v in fetch if "copybuffer" in k.lower() and "dpg" not in k)
+    copy_w = max(v for k, v in write if "copybuffer" in k.lower() and "dpg" not in k)
+    f_scale, w_scale = (COPY_BYTES / 1024.0) / copy_f, (COPY_BYTES / 1024.0) / copy_w
+    mine_f = [(k, v) for k, v in fetch if "dpg::" in k]
+    mine_w = [(k, v) for k, v in write if "dpg::" in k]
+    path = os.path.join(PROFILE_DIR, "skinny_wgrad_T16384_f32_pmc.txt")
+    with open(path, "w") as f:
+        f.write("HBM traffic of the skinny weight gradients (T=16384, FP32 out, planner splits), rocprofv3 PMC "
+                "on MI355X\ncommands:\n  %s\n" % command.replace("\n", "\n  "))
+        f.write("skinny_source_hash: %s\n" % skinny_source_hash())
+        f.write("calibration: 1 GiB device copy read %.1f KB / wrote %.1f KB -> scale fetch x%.4f, write x%.4f\n"
+                % (copy_f, copy_w, f_scale, w_scale))
+        i = 0
+        for K, N in SKINNY:
+            tot_f = tot_w = 0.0
+            names = []
+            while i < len(mine_f):
+                k, v = mine_f[i]
+                if names and "reduce" not in k:
+                    break
+                names.append(k.replace("void dpg::", "").split("(")[0])
+                tot_f += v * 1024.0 * f_scale
+                tot_w += mine_w[i][1] * 1024.0 * w_scale
+                i += 1
+                if "reduce" in k:
+                    break
+            alg = 2.0 * SKINNY_T * K + 2.0 * SKINNY_T * N + 4.0 * N * K
+            f.write("%d->%d: fetch %.4g B, write %.4g B, total %.4g B; algorithmic %.4g B (ratio %.3f); kernels: %s\n"
+                    % (K, N, tot_f, tot_w, tot_f + tot_w, alg, (tot_f + tot_w) / alg, " + ".join(names)))
+    print("wrote", path)
 
 
 def clock_load(seconds):
@@ -232,9 +311,19 @@ def summarize_busy(counter_csv, command, xcds=8, cus=256):
     print("wrote", path)
 
 
-def summarize_trace(stats_csv, command, out_name="bench_4096x12288_T16384_kernel_trace.txt"):
-    """Writes the kernel-trace summary (rocprofv3 --stats) under profiles/."""
+def summarize_trace(stats_csv, command, bench_log=None, out_name="bench_4096x12288_T16384_kernel_trace.txt"):
+    """Writes the kernel-trace summary (rocprofv3 --stats) under profiles/: all
+    kernels, then each pass's mean over the timed steps (the last --steps
+    dispatches of its BF16-output kernel) beside the HIP-event means that the
+    traced run's own bench line reported (bench_log: that run's output)."""
     import csv
+    m = re.search(r"--steps\s+(\d+)", command)
+    steps = int(m.group(1)) if m else 10
+    events = {}
+    if bench_log and os.path.exists(bench_log):
+        lines = [l for l in open(bench_log) if l.startswith("{")]
+        if lines:
+            events = {k: v["us_mean"] for k, v in json.loads(lines[-1])["passes"].items()}
     rows = list(csv.DictReader(open(stats_csv)))
     path = os.path.join(PROFILE_DIR, out_name)
     with open(path, "w") as f:
@@ -252,16 +341,19 @@ def summarize_trace(stats_csv, command, out_name="bench_4096x12288_T16384_kernel
         if os.path.exists(trace_csv):
             per = {}
             for r in csv.DictReader(open(trace_csv)):
-                if "gemm_fast_kernel<256, 256" in r["Kernel_Name"]:
-                    per.setdefault(r["Kernel_Name"], []).append(
-                        (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-            f.write("\nlast 5 dispatches (the timed steps; the first ones are warmups):\n")
-            for k, v in per.items():
-                last = v[-5:]
-                f.write("  %10.1f us avg  %s\n" % (sum(last) / len(last), k.replace("void ", "")[:90]))
+                for name, tag in PASS_KERNEL_TAG.items():
+                    if "gemm_fast_kernel<256, 256" in r["Kernel_Name"] and (", %s, 0," % tag) in r["Kernel_Name"]:
+                        per.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            f.write("\nper pass over the %d timed steps (the last %d dispatches of its BF16-output kernel; the first "
+                    "ones are warmups), against the HIP-event mean of the same run's bench line:\n" % (steps, steps))
+            for name, v in per.items():
+                last = v[-steps:]
+                f.write("  %-5s %10.1f us (trace)  %10s us (events)\n"
+                        % (name, sum(last) / len(last), events.get(name, "n/a")))
         f.write("\ngemm_fast_kernel<256, 256, 2, 4, A K-major, B K-major, OUT>: forward = <true, true>, "
                 "input gradient = <true, false>, weight gradient = <false, false>; 1.649e12 FLOP per launch.\n"
-                "skinny_wgrad_kernel and splitk_reduce_kernel: the skinny-N weight gradients (T=16384).\n")
+                "skinny_wgrad_kernel (N > 64, or forced small split counts), skinny_direct_kernel (N <= 64) and "
+                "splitk_reduce_kernel: the skinny-N weight gradients (T=16384 and 65537).\n")
     print("wrote", path)
 
 
@@ -415,16 +507,23 @@ def main():
                     help="run the forward GEMM in a loop for SECONDS (to read the clock under load)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"))
     ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "COMMAND"))
+    ap.add_argument("--bench-log", help="with --summarize-trace: output of the traced bench run")
     ap.add_argument("--summarize-busy", nargs=2, metavar=("COUNTER_CSV", "COMMAND"))
+    ap.add_argument("--profile-skinny", action="store_true",
+                    help="the skinny weight gradients once each after a 1 GiB calibration copy (for rocprofv3)")
+    ap.add_argument("--summarize-skinny-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"))
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
         return
     if args.summarize_trace:
-        summarize_trace(*args.summarize_trace)
+        summarize_trace(*args.summarize_trace, bench_log=args.bench_log)
         return
     if args.summarize_busy:
         summarize_busy(*args.summarize_busy)
+        return
+    if args.summarize_skinny_pmc:
+        summarize_skinny_pmc(*args.summarize_skinny_pmc)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -433,6 +532,9 @@ def main():
 
     if args.profile_run:
         profile_run()
+        return
+    if args.profile_skinny:
+        profile_skinny()
         return
     if args.clock_load:
         clock_load(args.clock_load)
