@@ -282,6 +282,7 @@ SKINNY_EXACT = [
     (65537, 104, 3968),  # two row blocks, N ragged, 256-column units, last unit half outside K
     (16400, 40, 1000),   # one row block, N ragged, last 128-column unit partial, 16 splits of
                          # 17 or 2 token blocks (one 16-token step per wave), last block 16 tokens
+    (16400, 104, 1000),  # the same with two row blocks (two LDS stages), N ragged, one iteration
 ]
 
 

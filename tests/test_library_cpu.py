@@ -94,9 +94,11 @@ def test_skinny_unit_shapes():
     assert tile(32640, 104, 4096, 1, 0) == "128x128x64"
     p = plan(2, 16400, 40, 1000, out=F32, det=1, split=0)
     assert p["tile"] == "64x128x64" and p["splits"] == "16" and p["kt_per_split"] == "17", p
+    p = plan(2, 16400, 104, 1000, out=F32, det=1, split=0)
+    assert p["tile"] == "128x128x64" and p["splits"] == "16" and p["kt_per_split"] == "17", p
     seen = set()
     for T, N, K in [(4031, 128, 4096), (16384, 48, 5120), (1025, 104, 1024), (16384, 128, 4096), (65537, 104, 3968),
-                    (16400, 40, 1000)]:
+                    (16400, 40, 1000), (16400, 104, 1000)]:
         for det, split in [(1, 0), (0, 1), (0, 2), (1, 3)]:
             seen.add(tile(T, N, K, det, split))
     assert seen == {"64x64x64", "64x128x64", "128x64x64", "128x128x64", "128x256x64"}
