@@ -382,6 +382,72 @@ def cpu_baseline(target_s=20.0):
                       % (rows, rows, dt)}
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_oracle_small():
+    """The FP64 oracle timed on the small workloads it finishes in seconds,
+    wall-clock milliseconds per pass with all host threads and with one: the
+    4096->1024 projection at T = 64 (BF16 operands) and the FP32 router
+    (E = 256, H = 4096) at T = 64 / 256 / 1024 (exact FP64 products)."""
+    import dpg_inputs
+    import oracle
+    n_all = oracle.num_threads()
+    jobs = []
+    x, w, dy = dpg_inputs.dense(64, 1024, 4096, seed_group=0)
+    jobs.append(("projection_4096x1024_T64", x, w, dy))
+    for T in (64, 256, 1024):
+        rx, rw, rdy = dpg_inputs.router(T, 256, 4096, seed_group=0)
+        jobs.append(("router_E256_H4096_T%d" % T, rx, rw, rdy))
+    out = {"cpu_model": cpu_model(), "threads_all": n_all, "unit": "ms per pass"}
+    for threads in (n_all, 1):
+        oracle.set_num_threads(threads)
+        key = "threads_%d" % threads
+        for name, a, b, g in jobs:
+            res = {}
+            for pname, fn in (("fwd", lambda: oracle.forward(a, b)), ("dgrad", lambda: oracle.dgrad(g, b)),
+                              ("wgrad", lambda: oracle.wgrad(g, a))):
+                t0 = time.perf_counter()
+                fn()
+                res[pname] = round((time.perf_counter() - t0) * 1e3, 1)
+            out.setdefault(name, {})[key] = res
+    oracle.set_num_threads(n_all)
+    return out
+
+
+def cold_cache_passes(passes, torch, reps=8):
+    """Each big pass timed alone after a 1 GiB device fill (a cold L2 and
+    Infinity Cache): median microseconds of `reps` runs, HIP events on the
+    launch stream around the pass only."""
+    import numpy as np
+    stream = torch.cuda.current_stream()
+    junk = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+    flop = 2.0 * T_BIG * N_BIG * K_BIG
+    out = {}
+    for name, fn in passes:
+        ts = []
+        for _ in range(reps):
+            junk.zero_()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e3)
+        us = float(np.median(ts))
+        out[name] = {"us_median": round(us, 1), "tflops": round(flop / us / 1e6, 1),
+                     "frac_peak": round(flop / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
+    del junk
+    return out
+
+
 def secondary_configs(dpg, dpg_inputs, torch, to_dev):
     """The other measured workloads, microseconds per call: the 4096->1024
     projection at T = 64 (BF16, deterministic), the FP32 router (E = 256,
@@ -608,6 +674,7 @@ def main():
     busy = read_mfma_busy(dominant)
     if busy:
         roofline["counters"] = busy
+    cold = cold_cache_passes(passes, torch)
 
     skinny = []
     if not args.skip_skinny:
@@ -643,6 +710,7 @@ def main():
     secondary = None if args.skip_secondary else secondary_configs(dpg, dpg_inputs, torch, to_dev)
 
     cpu = None if args.no_cpu_baseline else cpu_baseline()
+    cpu_small = None if args.no_cpu_baseline else cpu_oracle_small()
 
     line = {
         "metric": "TFLOP/s and % BF16 MFMA peak per pass, 4096->12288 T=16384; skinny wgrad GB/s",
@@ -662,10 +730,12 @@ def main():
                    "T": T_BIG, "N": N_BIG, "K": K_BIG, "global_batch": T_BIG, "parallelism": "single GPU"},
         "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "passes": per_pass,
+        "passes_cold_cache": cold,
         "skinny_wgrad": skinny,
         "other_workloads": secondary,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "cpu_oracle_small_configs": cpu_small,
         "kernel_source_hash": kernel_source_hash(),
     }
     print(json.dumps(line))

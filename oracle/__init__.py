@@ -75,10 +75,16 @@ class Oracle:
         lib.orc_f64_to_bf16_via_f32.argtypes = [vp, vp, i64]
         lib.orc_split_bf16x3.argtypes = [vp, vp, vp, i64]
         lib.orc_num_threads.restype = ip
+        lib.orc_set_num_threads.argtypes = [ip]
+        lib.orc_set_num_threads.restype = None
         self._lib = lib
 
     def num_threads(self):
         return self._lib.orc_num_threads()
+
+    def set_num_threads(self, n):
+        """OpenMP threads of later calls (timing only; results do not depend on it)."""
+        self._lib.orc_set_num_threads(int(n))
 
     def _matmul(self, M, N, R, a, asi, asr, b, bsr, bsj, mode):
         a_arr, adt = a
@@ -210,3 +216,7 @@ def split_bf16x3(a):
 
 def num_threads():
     return default().num_threads()
+
+
+def set_num_threads(n):
+    default().set_num_threads(n)

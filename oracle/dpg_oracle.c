@@ -164,3 +164,13 @@ int orc_num_threads(void) {
   return 1;
 #endif
 }
+
+/* Thread count for later calls (timing of the oracle on one thread). */
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  extern void omp_set_num_threads(int);
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

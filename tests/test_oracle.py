@@ -293,3 +293,23 @@ def test_pins_catch_planted_mistake(name, mutant_dir):
     lib = oracle.build(force=True, src=path, out=os.path.join(mutant_dir, name + ".so"))
     with pytest.raises(AssertionError):
         pin(oracle.Oracle(lib))
+
+
+def test_thread_count_does_not_change_results():
+    """Each output is one ascending FP64 sum computed by one thread, so the
+    thread count (the bench times the oracle on one thread and on all) cannot
+    change a bit of the result."""
+    x, w, dy = dpg_inputs.dense(37, 72, 200, seed_group=3)
+    rx, rw, rdy = dpg_inputs.router(19, 24, 256, seed_group=3)
+    n_all = oracle.num_threads()
+    try:
+        outs = []
+        for n in (n_all, 1):
+            oracle.set_num_threads(n)
+            assert oracle.num_threads() == n
+            outs.append([oracle.forward(x, w), oracle.dgrad(dy, w), oracle.wgrad(dy, x),
+                         oracle.forward(rx, rw, mode="bf16x3"), oracle.wgrad(rdy, rx)])
+    finally:
+        oracle.set_num_threads(n_all)
+    for a, b in zip(*outs):
+        assert np.array_equal(a.view(np.int64), b.view(np.int64))
