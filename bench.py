@@ -319,6 +319,8 @@ def summarize_trace(stats_csv, command, bench_log=None, out_name="bench_4096x122
     import csv
     m = re.search(r"--steps\s+(\d+)", command)
     steps = int(m.group(1)) if m else 10
+    m = re.search(r"--warmup\s+(\d+)", command)
+    warmup = int(m.group(1)) if m else 3
     events = {}
     if bench_log and os.path.exists(bench_log):
         lines = [l for l in open(bench_log) if l.startswith("{")]
@@ -344,10 +346,11 @@ def summarize_trace(stats_csv, command, bench_log=None, out_name="bench_4096x122
                 for name, tag in PASS_KERNEL_TAG.items():
                     if "gemm_fast_kernel<256, 256" in r["Kernel_Name"] and (", %s, 0," % tag) in r["Kernel_Name"]:
                         per.setdefault(name, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-            f.write("\nper pass over the %d timed steps (the last %d dispatches of its BF16-output kernel; the first "
-                    "ones are warmups), against the HIP-event mean of the same run's bench line:\n" % (steps, steps))
+            f.write("\nper pass over the %d timed steps (dispatches %d..%d of its BF16-output kernel: after the %d "
+                    "warmups, before the cold-cache runs), against the HIP-event mean of the same run's bench line:\n"
+                    % (steps, warmup + 1, warmup + steps, warmup))
             for name, v in per.items():
-                last = v[-steps:]
+                last = v[warmup:warmup + steps]
                 f.write("  %-5s %10.1f us (trace)  %10s us (events)\n"
                         % (name, sum(last) / len(last), events.get(name, "n/a")))
         f.write("\ngemm_fast_kernel<256, 256, 2, 4, A K-major, B K-major, OUT>: forward = <true, true>, "
