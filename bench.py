@@ -451,6 +451,63 @@ def cold_cache_passes(passes, torch, reps=8):
     return out
 
 
+def config3_more(dpg, torch, X, W, DY, Y, DX, DW, passes):
+    """More of the 4096->12288 workload (event means over 5 calls after 2
+    warmups): the three passes at the ragged T = 16231 (row views of the same
+    operands), the input gradient with FP32 output at T = 16384, and the
+    step (three passes) as one captured HIP graph against its eager time
+    (medians of three alternating rounds)."""
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps=5):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def entry(us, T):
+        flop = 2.0 * T * N_BIG * K_BIG
+        return {"us": round(us, 1), "tflops": round(flop / us / 1e6, 1),
+                "frac_peak": round(flop / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
+    out = {}
+    Tr = 16231
+    xr, dyr, yr, dxr = X[:Tr], DY[:Tr], Y[:Tr], DX[:Tr]
+    out["T16231_bf16"] = {
+        "fwd": entry(timed(lambda: dpg.dpg_forward(xr, W, out=yr)), Tr),
+        "dgrad": entry(timed(lambda: dpg.dpg_dgrad(dyr, W, out=dxr)), Tr),
+        "wgrad": entry(timed(lambda: dpg.dpg_wgrad(dyr, xr, out=DW)), Tr)}
+    dxf = torch.empty((T_BIG, K_BIG), dtype=torch.float32, device=X.device)
+    out["T16384_dgrad_f32_out"] = entry(timed(lambda: dpg.dpg_dgrad(DY, W, out=dxf)), T_BIG)
+    del dxf
+    # the step captured once, replayed; eager time of the same three calls
+    eager = timed(lambda: [fn() for _, fn in passes])
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for _, fn in passes:
+            fn()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _, fn in passes:
+            fn()
+    import numpy as np
+    eg, gr = [eager], [timed(g.replay)]
+    for _ in range(2):  # alternate, so clock drift does not favour either mode
+        eg.append(timed(lambda: [fn() for _, fn in passes]))
+        gr.append(timed(g.replay))
+    out["step_ms"] = {"eager": round(float(np.median(eg)) / 1e3, 3), "graph": round(float(np.median(gr)) / 1e3, 3),
+                      "rounds": 3}
+    return out
+
+
 def secondary_configs(dpg, dpg_inputs, torch, to_dev):
     """The other measured workloads, microseconds per call: the 4096->1024
     projection at T = 64 (BF16, deterministic), the FP32 router (E = 256,
@@ -678,6 +735,7 @@ def main():
     if busy:
         roofline["counters"] = busy
     cold = cold_cache_passes(passes, torch)
+    more = config3_more(dpg, torch, X, W, DY, Y, DX, DW, passes)
 
     skinny = []
     if not args.skip_skinny:
@@ -734,6 +792,7 @@ def main():
         "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "passes": per_pass,
         "passes_cold_cache": cold,
+        "projection_4096x12288_more": more,
         "skinny_wgrad": skinny,
         "other_workloads": secondary,
         "roofline": roofline,
