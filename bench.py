@@ -454,9 +454,10 @@ def cold_cache_passes(passes, torch, reps=8):
 def config3_more(dpg, torch, X, W, DY, Y, DX, DW, passes):
     """More of the 4096->12288 workload (event means over 5 calls after 2
     warmups): the three passes at the ragged T = 16231 (row views of the same
-    operands), the input gradient with FP32 output at T = 16384, and the
-    step (three passes) as one captured HIP graph against its eager time
-    (medians of three alternating rounds)."""
+    operands), an A/A control (the forward timed again after the plan cache
+    is cleared and the plan rebuilt), the input gradient with FP32 output at
+    T = 16384, and the step (three passes) as one captured HIP graph against
+    its eager time (medians of three alternating rounds)."""
     stream = torch.cuda.current_stream()
 
     def timed(fn, reps=5):
@@ -482,6 +483,12 @@ def config3_more(dpg, torch, X, W, DY, Y, DX, DW, passes):
         "fwd": entry(timed(lambda: dpg.dpg_forward(xr, W, out=yr)), Tr),
         "dgrad": entry(timed(lambda: dpg.dpg_dgrad(dyr, W, out=dxr)), Tr),
         "wgrad": entry(timed(lambda: dpg.dpg_wgrad(dyr, xr, out=DW)), Tr)}
+    # A/A control: the forward again from a plan built anew after clearing the
+    # plan cache (a second, independently planned instance of the same call)
+    first = timed(lambda: dpg.dpg_forward(X, W, out=Y))
+    dpg.clear_plan_cache()
+    second = timed(lambda: dpg.dpg_forward(X, W, out=Y))
+    out["aa_control_fwd_us"] = {"cached_plan": round(first, 1), "replanned": round(second, 1)}
     dxf = torch.empty((T_BIG, K_BIG), dtype=torch.float32, device=X.device)
     out["T16384_dgrad_f32_out"] = entry(timed(lambda: dpg.dpg_dgrad(DY, W, out=dxf)), T_BIG)
     del dxf
