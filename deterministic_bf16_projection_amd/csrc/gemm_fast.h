@@ -318,10 +318,12 @@ __device__ __forceinline__ void sched_step() {
 }
 
 // Scheduling of one k-step: the pinned interleave above, or (IGLP) the
-// compiler's own MFMA / DS interleave strategy (iglp_opt(0)).  The eight-wave
-// forward layout (both operands K-major) measured 1.7% faster with the latter
-// (five interleaved repeats of the 4096 -> 12288 step, every pair faster), the
-// gradient layouts 3-4% slower, so only that layout uses it.
+// compiler's own MFMA / DS interleave strategy (iglp_opt(0)).  The forward
+// layout (both operands K-major) measured faster with the latter: the
+// eight-wave 256x256 tile by 1.7% (five interleaved repeats of the 4096 ->
+// 12288 step, every pair faster), the four-wave 128x128 tile by ~7% (4096 ->
+// 512 at 16384 tokens, FP32 out); the gradient layouts were 3-4% slower, so
+// only the forward layout uses it (BF16x3 tiles keep the pinned order).
 template <bool IGLP, int NM, int NR, int NW, int NV>
 __device__ __forceinline__ void sched_kstep() {
   if constexpr (IGLP)
@@ -413,7 +415,7 @@ struct FastGemm {
   // pass (both operands K-major) register staging is 4% faster.
   static constexpr bool DMA = !X3 && ROLE == ROLE_A && A_KMAJ && !B_KMAJ;
   // k-step scheduling by the compiler's interleave strategy (see sched_kstep)
-  static constexpr bool IGLP = !X3 && ROLE != ROLE_BOTH && A_KMAJ && B_KMAJ;
+  static constexpr bool IGLP = !X3 && A_KMAJ && B_KMAJ;
 
   // Accumulators hold the transposed product: acc[i][j] is the 32x32 block
   // D[n][m] = sum_k B(n,k) A(m,k), so that lane l owns output row m = l % 32
