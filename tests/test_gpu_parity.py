@@ -304,6 +304,37 @@ def test_skinny_exact_integer(T, N, K):
                 np.testing.assert_array_equal(host_bits(got), oracle.f64_to_bf16(ref))
 
 
+# Skinny weight gradients through row strides wider than the rows: dY and X
+# are column slices of wider buffers, dW is written into a column slice of a
+# NaN-filled buffer.  The planner's plans take the kernel without LDS staging
+# (16400x40x1000), the two-stage LDS kernel (16384x128x4096) and the
+# single-stage LDS kernel (4031x64x4096, and every shape with the forced split
+# count of 2).
+@pytest.mark.parametrize("T,N,K", [(16400, 40, 1000), (16384, 128, 4096), (4031, 64, 4096)])
+def test_skinny_padded_strides(T, N, K):
+    x, _, dy = dpg_inputs.dense(T, N, K, seed_group=12, kind="int")
+
+    def padded(bits, extra):
+        t = torch.zeros((bits.shape[0], bits.shape[1] + extra), dtype=torch.bfloat16, device="cuda")
+        t[:, :bits.shape[1]] = dev_bf16(bits)
+        return t[:, :bits.shape[1]]
+    X, DY = padded(x, 72), padded(dy, 24)
+    assert X.stride(0) == K + 72 and DY.stride(0) == N + 24
+    ii, jj = sample_positions(N, K, 3000, seed=T + 1)
+    ref = oracle.wgrad(dy, x, rows=ii, cols=jj)
+    ti, tj = torch.from_numpy(ii).cuda(), torch.from_numpy(jj).cuda()
+    for det, split in [(True, 0), (False, 2)]:
+        plan = dpg.parse_plan(dpg.plan_describe(dpg.PASS_WGRAD, T, N, K, torch.float32, det, split))
+        assert plan["kernel"] == "skinny", plan
+        big = torch.full((N + 2, K + 40), float("nan"), dtype=torch.float32, device="cuda")
+        view = big[1:N + 1, 8:8 + K]
+        _run("wgrad", DY, X, torch.float32, det=det, split=split, out=view)
+        np.testing.assert_array_equal(host_f64(view[ti, tj]), ref)
+        mask = torch.ones_like(big, dtype=torch.bool)
+        mask[1:N + 1, 8:8 + K] = False
+        assert torch.isnan(big[mask]).all()
+
+
 # ------------------------------------------- checkpointed step 2fwd + bwd --
 @pytest.mark.parametrize("N", [1024, 512])
 def test_checkpointed_step(N):
