@@ -14,6 +14,7 @@
 #include "gemm_kernel.h"
 #include "skinny_wgrad.h"
 #include "skinny_direct.h"
+#include "skinny_lds.h"
 #include "planner.h"
 
 namespace dpg {
@@ -109,17 +110,19 @@ SkinnyFn lookup_skinny_kernel(int nb, int cb, int out_kind) {
                                        &skinny_direct_kernel<OUT_PARTIAL>};
     return out_kind >= 0 && out_kind <= 2 ? direct[out_kind] : nullptr;
   }
-  // LDS-staged kernel: column blocks 1, 2 or 4 (one row block: 1 only)
-  static const SkinnyFn table[2][3][3] = {
-      {{SkinnyRow<1, 1>::fns[0], SkinnyRow<1, 1>::fns[1], SkinnyRow<1, 1>::fns[2]},
-       {nullptr, nullptr, nullptr},
-       {nullptr, nullptr, nullptr}},
-      {{SkinnyRow<2, 1>::fns[0], SkinnyRow<2, 1>::fns[1], SkinnyRow<2, 1>::fns[2]},
-       {SkinnyRow<2, 2>::fns[0], SkinnyRow<2, 2>::fns[1], SkinnyRow<2, 2>::fns[2]},
-       {SkinnyRow<2, 4>::fns[0], SkinnyRow<2, 4>::fns[1], SkinnyRow<2, 4>::fns[2]}},
+  // two row blocks and 128-column units: operands fetched straight into LDS
+  if (nb == 2 && cb == 2) {
+    static const SkinnyFn lds[3] = {&skinny_lds_kernel<OUT_BF16>, &skinny_lds_kernel<OUT_F32>,
+                                    &skinny_lds_kernel<OUT_PARTIAL>};
+    return out_kind >= 0 && out_kind <= 2 ? lds[out_kind] : nullptr;
+  }
+  // 64-column units: the LDS-staged kernel with register transposes
+  static const SkinnyFn table[2][3] = {
+      {SkinnyRow<1, 1>::fns[0], SkinnyRow<1, 1>::fns[1], SkinnyRow<1, 1>::fns[2]},
+      {SkinnyRow<2, 1>::fns[0], SkinnyRow<2, 1>::fns[1], SkinnyRow<2, 1>::fns[2]},
   };
-  if (nb < 1 || nb > 2 || (cb != 1 && cb != 2 && cb != 4) || out_kind < 0 || out_kind > 2) return nullptr;
-  return table[nb - 1][cb == 4 ? 2 : cb - 1][out_kind];
+  if (nb < 1 || nb > 2 || cb != 1 || out_kind < 0 || out_kind > 2) return nullptr;
+  return table[nb - 1][out_kind];
 }
 
 int tile_threads(int tile) { return kTiles[tile].threads; }

@@ -125,15 +125,11 @@ bool make_plan(const PlanKey& key, Plan* p) {
     p->tiles_m = (int)cdiv(p->M, 64);
     p->tiles_n = (int)cdiv(p->N, 64);
     p->kt_total = (int)cdiv(p->K, 64);  // 64-token blocks
-    // Two row blocks over long token ranges: 256-column units, when they still
-    // give every CU one and each split covers at least 32 token blocks (2048
-    // tokens); a dY tile then serves twice the columns, which pays for the
-    // twice as many split planes only on long ranges (4096->128: 140 -> 123 us
-    // at 65537 tokens; 3% slower at 16384).
-    const int64_t wunits = cdiv(p->N, 256);
-    const int64_t wsplits = std::min<int64_t>((key.cus + wunits / 2) / wunits, std::max<int64_t>(1, p->kt_total / 16));
-    const bool wide = p->M > 64 && key.split_req == 0 && wunits * wsplits >= key.cus && p->kt_total >= 32 * wsplits;
-    const int64_t units = wide ? wunits : cdiv(p->N, 128);
+    // (256-column units for two row blocks over long token ranges were faster
+    // with the register-staged kernel; with operands fetched straight into LDS
+    // 128-column units win there too: 4096->128 at 65537 tokens 118-120 ->
+    // 112-115 us, at 32768 66 -> 58 us.)
+    const int64_t units = cdiv(p->N, 128);
     int64_t s;
     if (key.split_req > 0) {
       s = key.split_req;
@@ -145,7 +141,7 @@ bool make_plan(const PlanKey& key, Plan* p) {
     p->kt_per_split = (int)cdiv(p->kt_total, s);
     p->splits = (int)cdiv(p->kt_total, p->kt_per_split);
     // 64-column units when 128-column ones would leave more than half the CUs idle
-    p->skinny_cols = wide ? 256 : (units * p->splits * 2 >= key.cus ? 128 : 64);
+    p->skinny_cols = units * p->splits * 2 >= key.cus ? 128 : 64;
     p->group_m = 1;
     p->grid = cdiv(p->N, p->skinny_cols) * p->splits;
     p->ws_bytes = p->splits > 1 ? (size_t)p->splits * (size_t)p->M * (size_t)p->N * 4u : 0;

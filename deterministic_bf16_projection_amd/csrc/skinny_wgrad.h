@@ -4,20 +4,16 @@
 //
 // Work unit = (all N rows, a block of CB * 64 columns of K, token split).  A
 // workgroup has 8 waves arranged as NB row blocks x CB column blocks x TG token
-// groups (NB * CB * TG = 8; NB = 1 for N <= 64, 2 for N <= 128; CB = 2, or 1
-// when a small forced split count leaves too few units, or 4 with two row
-// blocks over long token ranges, where each dY tile then serves 256 columns;
-// one row block with 128-column units runs skinny_direct.h instead),
+// groups (NB * CB * TG = 8; NB = 1 for N <= 64, 2 for N <= 128).  The library
+// runs it with CB = 1, i.e. 64-column units, which the planner picks when a
+// small forced split count would leave too few 128-column units; 128-column
+// units run skinny_direct.h (N <= 64) or skinny_lds.h (N <= 128),
 // each wave owning a 64 x 64 block of dW.  Per iteration, token group g takes the unit's 64-token
 // block (iteration * TG + g): its X tiles (64 tokens x 64 columns) and dY tiles
 // (64 tokens x 64 rows) are fetched once with 16-byte buffer loads (rows past T
 // read as zero), transposed in registers (8x8 BF16 blocks) and written
 // K-contiguous into LDS, where the waves that share a tile read it.  The loads
-// of the next iteration are issued before this iteration's MFMAs.  Where two
-// sets of tiles fit in LDS (two 64-row blocks, 128 or 256 columns), the next
-// iteration's tiles are written while this one's are read, one barrier per
-// iteration, and the two waves of each SIMD run the halves in opposite orders
-// (one transposes and writes while the other issues MFMAs).  At the end
+// of the next iteration are issued before this iteration's MFMAs.  At the end
 // the TG partial tiles of each output block are summed in LDS in token-group
 // order 0..TG-1 and written once: to the output (one token split) or to the
 // FP32 workspace plane of the split.
@@ -42,18 +38,13 @@ template <int NB, int CB, int OUT>
 __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
   constexpr int W = 8;
   constexpr int TG = W / (NB * CB);     // token groups
-  static_assert((NB == 1 || NB == 2) && (CB == 1 || CB == 2 || (CB == 4 && NB == 2)), "row and column blocks");
+  static_assert((NB == 1 || NB == 2) && (CB == 1 || CB == 2), "row and column blocks");
   constexpr int TILE = 4096;            // BF16 elements of one transposed 64x64 tile
   constexpr int X_TILES = CB * TG, Y_TILES = NB * TG;
   constexpr int RED_LD = 68;            // FP32 row stride of the reduction buffer
   constexpr int STAGE_ELEMS = (X_TILES + Y_TILES) * TILE;
-  // Two LDS stages where they fit in the 160 KB of a CU: the tiles of the next
-  // iteration are written while this one's are read, with one barrier per
-  // iteration, so waves staging and waves issuing MFMAs overlap.
-  constexpr bool DB = 2 * STAGE_ELEMS * 2 <= 160 * 1024;
-  constexpr int BUF_ELEMS = DB ? STAGE_ELEMS : 0;  // offset of the second stage
   constexpr int RED_FLOATS = W * 64 * RED_LD;
-  constexpr int SMEM_FLOATS = ((DB ? 2 : 1) * STAGE_ELEMS / 2 > RED_FLOATS) ? (DB ? 2 : 1) * STAGE_ELEMS / 2 : RED_FLOATS;
+  constexpr int SMEM_FLOATS = (STAGE_ELEMS / 2 > RED_FLOATS) ? STAGE_ELEMS / 2 : RED_FLOATS;
   __shared__ __attribute__((aligned(16))) float smem_f[SMEM_FLOATS];
   __bf16* smem = (__bf16*)smem_f;
 
@@ -80,15 +71,12 @@ __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
   // columns; wave w fetches tile w + 8 r in round r (X tiles first, then dY
   // tiles).  A tile is 8 x 8 sub-blocks of 8x8: lane (kc, sb) = (lane / 8,
   // lane % 8) owns token rows kc*8.. and columns sb*8.., so the 8 lanes of one
-  // token row read 128 contiguous bytes.  With two LDS stages (N > 64 with 128-
-  // or 256-column units) the loads run two iterations ahead of the MFMAs in one
-  // register buffer; otherwise, with one round (one tile per wave), two
-  // iterations ahead in two register buffers, and with two rounds one ahead.
+  // token row read 128 contiguous bytes.  With one round (N > 64 and 128-column
+  // units) the loads run two iterations ahead in two register buffers; with two
+  // rounds, one iteration ahead.
   constexpr int TILES = X_TILES + Y_TILES;
   constexpr int ROUNDS = (TILES + W - 1) / W;
-  // With two LDS stages one register buffer suffices (the tiles of iteration
-  // it + 2 are fetched while it runs); two would exceed the register budget.
-  constexpr int AHEAD = DB ? 1 : (ROUNDS == 1 ? 2 : 1);
+  constexpr int AHEAD = ROUNDS == 1 ? 2 : 1;
   const int kc = lane >> 3, sb = lane & 7;
   // Lanes with odd kc hold transposed column m ^ 1 in slot m (a per-lane choice
   // of byte selectors), so that the 16 lanes of one LDS write phase cover rows
@@ -173,8 +161,8 @@ __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
       }
     }
   };
-  auto stage = [&](const u32x4(&gb)[ROUNDS][8], int buf) {
-    int o = lds0 + buf;
+  auto stage = [&](const u32x4(&gb)[ROUNDS][8]) {
+    int o = lds0;
     asm volatile("" : "+v"(o));  // form the slot offsets here, not in the loop preheader
 #pragma unroll
     for (int r = 0; r < ROUNDS; ++r) {
@@ -186,86 +174,35 @@ __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
       }
     }
   };
-  auto compute = [&](int buf) {
+  auto compute = [&]() {
+    __syncthreads();  // shared tiles complete
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       bf16x8 fa[2], fb[2];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i] = as_bf16x8(*(const u32x4*)(y_tile + buf + (i * 32 + lr) * 64 + koff[s ^ (2 * i)]));
+      for (int i = 0; i < 2; ++i) fa[i] = as_bf16x8(*(const u32x4*)(y_tile + (i * 32 + lr) * 64 + koff[s ^ (2 * i)]));
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        fb[j] = as_bf16x8(*(const u32x4*)(x_tile + buf + (j * 32 + lr) * 64 + koff[s ^ (2 * j)]));
+      for (int j = 0; j < 2; ++j) fb[j] = as_bf16x8(*(const u32x4*)(x_tile + (j * 32 + lr) * 64 + koff[s ^ (2 * j)]));
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(fb[j], fa[i], acc[i][j]);
     }
+    __syncthreads();  // tiles consumed before the next iteration overwrites them
   };
 
-  // Iteration it is staged from register buffer it % AHEAD, which is refilled
-  // with iteration it + AHEAD right after staging (past the end: no memory
-  // access).
+  // iteration it is staged from buffer it % AHEAD; the buffer is refilled with
+  // iteration it + AHEAD right after staging (past the end: no memory access)
 #pragma unroll
   for (int b = 0; b < AHEAD; ++b) load(gbuf[b], b);
-  if constexpr (DB) {
-    // iteration it reads LDS stage it % 2; the barrier closing iteration it - 1
-    // makes stage it % 2 complete and stage (it + 1) % 2 free to overwrite
-    stage(gbuf[0], 0);
-    load(gbuf[0], AHEAD);
-    __syncthreads();
-    // The two waves of a SIMD (w and w + 4) take the two halves of an
-    // iteration in opposite orders, so one stages while the other issues MFMAs.
-    const bool stage_first = wave >= 4;
-    for (int it = 0; it < n_iter; it += 2) {
-      if (stage_first) {
-        if (it + 1 < n_iter) {
-          stage(gbuf[AHEAD - 1], BUF_ELEMS);
-          load(gbuf[AHEAD - 1], it + 1 + AHEAD);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep the halves apart (register pressure)
-        compute(0);
-      } else {
-        compute(0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (it + 1 < n_iter) {
-          stage(gbuf[AHEAD - 1], BUF_ELEMS);
-          load(gbuf[AHEAD - 1], it + 1 + AHEAD);
-        }
-      }
-      __syncthreads();
-      if (it + 1 >= n_iter) break;
-      if (stage_first) {
-        if (it + 2 < n_iter) {
-          stage(gbuf[0], 0);
-          load(gbuf[0], it + 2 + AHEAD);
-        }
-        __builtin_amdgcn_sched_barrier(0);  // keep the halves apart (register pressure)
-        compute(BUF_ELEMS);
-      } else {
-        compute(BUF_ELEMS);
-        __builtin_amdgcn_sched_barrier(0);
-        if (it + 2 < n_iter) {
-          stage(gbuf[0], 0);
-          load(gbuf[0], it + 2 + AHEAD);
-        }
-      }
-      __syncthreads();
-    }
-  } else {
-    for (int it = 0; it < n_iter; it += 2) {
-      stage(gbuf[0], 0);
-      load(gbuf[0], it + AHEAD);
-      __syncthreads();  // shared tiles complete
-      compute(0);
-      __syncthreads();  // tiles consumed before the next iteration overwrites them
-      if (it + 1 >= n_iter) break;
-      stage(gbuf[AHEAD - 1], 0);
-      load(gbuf[AHEAD - 1], it + 1 + AHEAD);
-      __syncthreads();
-      compute(0);
-      __syncthreads();
-    }
+  for (int it = 0; it < n_iter; it += 2) {
+    stage(gbuf[0]);
+    load(gbuf[0], it + AHEAD);
+    compute();
+    if (it + 1 >= n_iter) break;
+    stage(gbuf[AHEAD - 1]);
+    load(gbuf[AHEAD - 1], it + 1 + AHEAD);
+    compute();
   }
 
   // ---- fixed-order reduction over the token groups: acc[i][j] holds D[k][n];

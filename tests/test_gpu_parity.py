@@ -269,20 +269,19 @@ def test_skinny_wgrad(skinny_x, T, K, N):
 
 
 # Exact-integer inputs through the skinny kernels: one and two 64-row blocks of
-# dW, 64-, 128- and 256-column units (auto plans use 128 columns when enough
-# units exist, 256 for two row blocks over long token ranges; forced small
-# split counts use 64), ragged token tails.  One row block with 128-column
-# units runs the kernel without LDS staging (16384x48x5120, 16400x40x1000).
+# dW with 128-column units (auto plans with enough units: operands straight from
+# registers for one row block, fetched straight into LDS for two) and 64-column
+# units (forced small split counts: the LDS-staged kernel), ragged token tails.
 # (The planner's choices for these shapes are checked on the CPU.)
 SKINNY_EXACT = [
     (4031, 128, 4096),   # two row blocks; 63 token blocks, last holds 63
     (16384, 48, 5120),   # one row block, ragged N inside the block
     (1025, 104, 1024),   # two row blocks, N ragged; 17 token blocks, last holds 1
     (16384, 128, 4096),  # two row blocks, 128-column units
-    (65537, 104, 3968),  # two row blocks, N ragged, 256-column units, last unit half outside K
+    (65537, 104, 3968),  # two row blocks, N ragged, 31 units of 128 columns, 16 splits
     (16400, 40, 1000),   # one row block, N ragged, last 128-column unit partial, 16 splits of
                          # 17 or 2 token blocks (one 16-token step per wave), last block 16 tokens
-    (16400, 104, 1000),  # the same with two row blocks (two LDS stages), N ragged, one iteration
+    (16400, 104, 1000),  # the same with two row blocks, N ragged, 2 or 17 blocks a split
 ]
 
 
@@ -306,10 +305,9 @@ def test_skinny_exact_integer(T, N, K):
 
 # Skinny weight gradients through row strides wider than the rows: dY and X
 # are column slices of wider buffers, dW is written into a column slice of a
-# NaN-filled buffer.  The planner's plans take the kernel without LDS staging
-# (16400x40x1000), the two-stage LDS kernel (16384x128x4096) and the
-# single-stage LDS kernel (4031x64x4096, and every shape with the forced split
-# count of 2).
+# NaN-filled buffer.  The planner's plans take the register-direct kernel
+# (16400x40x1000), the LDS-fetching kernel (16384x128x4096) and the LDS-staged
+# kernel (4031x64x4096, and every shape with the forced split count of 2).
 @pytest.mark.parametrize("T,N,K", [(16400, 40, 1000), (16384, 128, 4096), (4031, 64, 4096)])
 def test_skinny_padded_strides(T, N, K):
     x, _, dy = dpg_inputs.dense(T, N, K, seed_group=12, kind="int")

@@ -72,10 +72,10 @@ def test_forced_split_one():
 def test_skinny_unit_shapes():
     """Skinny weight gradients: 128-column units when they give at least half
     as many workgroups as CUs, 64-column units otherwise (forced small split
-    counts), 256-column units for two row blocks over long token ranges; one or
-    two 64-row blocks of dW (one row block with 128-column units runs the
-    kernel without LDS staging).  The exact-integer GPU shapes together reach
-    all six kernel variants."""
+    counts); one or two 64-row blocks of dW.  128-column units run the kernels
+    without register staging (one row block: operands straight from registers;
+    two: operands fetched straight into LDS), 64-column units the LDS-staged
+    kernel.  The exact-integer GPU shapes together reach all four variants."""
     def tile(T, N, K, det, split):
         p = plan(2, T, N, K, out=F32, det=det, split=split)
         assert p["kernel"] == "skinny", p
@@ -85,13 +85,12 @@ def test_skinny_unit_shapes():
     assert tile(16384, 64, 4096, 0, 2) == "64x64x64"
     assert tile(16384, 128, 4096, 0, 1) == "128x64x64"
     assert tile(16384, 48, 5120, 1, 0) == "64x128x64"
-    # 256-column units: two row blocks, at least 2048 tokens per split, a unit per CU
-    assert tile(65537, 128, 4096, 1, 0) == "128x256x64"
+    # long token ranges keep 128-column units (with the LDS-fetching kernel they
+    # are faster than 256-column ones)
+    assert tile(65537, 128, 4096, 1, 0) == "128x128x64"
     assert tile(65537, 64, 4096, 1, 0) == "64x128x64"
     assert tile(65537, 128, 4096, 0, 2) == "128x64x64"
-    assert tile(16384, 128, 4096, 1, 0) == "128x128x64"
-    assert tile(32768, 104, 4096, 1, 0) == "128x256x64"
-    assert tile(32640, 104, 4096, 1, 0) == "128x128x64"
+    assert tile(32768, 104, 4096, 1, 0) == "128x128x64"
     p = plan(2, 16400, 40, 1000, out=F32, det=1, split=0)
     assert p["tile"] == "64x128x64" and p["splits"] == "16" and p["kt_per_split"] == "17", p
     p = plan(2, 16400, 104, 1000, out=F32, det=1, split=0)
@@ -101,7 +100,7 @@ def test_skinny_unit_shapes():
                     (16400, 40, 1000), (16400, 104, 1000)]:
         for det, split in [(1, 0), (0, 1), (0, 2), (1, 3)]:
             seen.add(tile(T, N, K, det, split))
-    assert seen == {"64x64x64", "64x128x64", "128x64x64", "128x128x64", "128x256x64"}
+    assert seen == {"64x64x64", "64x128x64", "128x64x64", "128x128x64"}
 
 
 def test_medium_projection_plans():
