@@ -40,6 +40,7 @@ SKINNY_RUNS = [(16384, [(True, 0), (False, 1), (False, 2)]), (65537, [(True, 0)]
 SKINNY_T = 16384
 SKINNY_SOURCES = ["deterministic_bf16_projection_amd/csrc/skinny_wgrad.h",
                   "deterministic_bf16_projection_amd/csrc/skinny_direct.h",
+                  "deterministic_bf16_projection_amd/csrc/skinny_lds.h",
                   "deterministic_bf16_projection_amd/csrc/gemm_kernel.h"]
 KERNEL_SOURCES = ["deterministic_bf16_projection_amd/csrc/gemm_fast.h",
                   "deterministic_bf16_projection_amd/csrc/gemm_kernel.h",
