@@ -110,19 +110,18 @@ SkinnyFn lookup_skinny_kernel(int nb, int cb, int out_kind) {
                                        &skinny_direct_kernel<OUT_PARTIAL>};
     return out_kind >= 0 && out_kind <= 2 ? direct[out_kind] : nullptr;
   }
-  // two row blocks and 128-column units: operands fetched straight into LDS
-  if (nb == 2 && cb == 2) {
-    static const SkinnyFn lds[3] = {&skinny_lds_kernel<OUT_BF16>, &skinny_lds_kernel<OUT_F32>,
-                                    &skinny_lds_kernel<OUT_PARTIAL>};
-    return out_kind >= 0 && out_kind <= 2 ? lds[out_kind] : nullptr;
+  // two row blocks, 128- or 64-column units: operands fetched straight into LDS
+  if (nb == 2 && (cb == 1 || cb == 2)) {
+    static const SkinnyFn lds[2][3] = {
+        {&skinny_lds_kernel<1, OUT_BF16>, &skinny_lds_kernel<1, OUT_F32>, &skinny_lds_kernel<1, OUT_PARTIAL>},
+        {&skinny_lds_kernel<2, OUT_BF16>, &skinny_lds_kernel<2, OUT_F32>, &skinny_lds_kernel<2, OUT_PARTIAL>}};
+    return out_kind >= 0 && out_kind <= 2 ? lds[cb - 1][out_kind] : nullptr;
   }
-  // 64-column units: the LDS-staged kernel with register transposes
-  static const SkinnyFn table[2][3] = {
-      {SkinnyRow<1, 1>::fns[0], SkinnyRow<1, 1>::fns[1], SkinnyRow<1, 1>::fns[2]},
-      {SkinnyRow<2, 1>::fns[0], SkinnyRow<2, 1>::fns[1], SkinnyRow<2, 1>::fns[2]},
-  };
-  if (nb < 1 || nb > 2 || cb != 1 || out_kind < 0 || out_kind > 2) return nullptr;
-  return table[nb - 1][out_kind];
+  // one row block and 64-column units (forced small split counts): the
+  // LDS-staged kernel with register transposes (the LDS-fetching kernel, whose
+  // second row block would read zeros, measured 11% slower there)
+  if (nb == 1 && cb == 1 && out_kind >= 0 && out_kind <= 2) return SkinnyRow<1, 1>::fns[out_kind];
+  return nullptr;
 }
 
 int tile_threads(int tile) { return kTiles[tile].threads; }

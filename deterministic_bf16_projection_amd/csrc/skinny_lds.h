@@ -4,22 +4,23 @@
 // X[T, K] is read once from HBM; the pass is bandwidth-bound, and what limits
 // it is how many bytes of X each CU keeps in flight.
 //
-// Work unit = (128 columns of K, token split of whole 64-token blocks); one
-// 64-token block per iteration.  The 8 waves are 2 row blocks x 2 column
-// blocks x 2 k-step halves: wave (nb, cb, ks) owns the 64 x 64 block (rows
-// 64 nb.., columns 64 cb..) of dW over k-steps 2 ks and 2 ks + 1 of every
-// block (16 tokens each).
+// Work unit = (CB * 64 columns of K, token split of whole 64-token blocks);
+// one 64-token block per iteration.  CB = 2 (128-column units, the planner's
+// plans) or 1 (64-column units, forced small split counts).  The 8 waves are
+// 2 row blocks x CB column blocks x 4 / CB k-step groups: wave (nb, cb, ks)
+// owns the 64 x 64 block (rows 64 nb.., columns 64 cb..) of dW over CB of the
+// block's four 16-token k-steps (k-steps CB ks ..).
 //
-// Staging without registers: a stage holds the block's two X tiles and two dY
+// Staging without registers: a stage holds the block's CB X tiles and two dY
 // tiles (64 tokens x 64 columns / rows each, row-major as in memory, 128 B a
-// token row, 32 KB in all) and is filled by buffer_load ... lds, 1 KB (8 token
-// rows) per instruction, 4 instructions per wave.  The 16-byte chunk c of token
+// token row, 24 or 32 KB in all) and is filled by buffer_load ... lds, 1 KB (8
+// token rows) per instruction, CB + 2 instructions per wave.  The 16-byte chunk c of token
 // row r sits at chunk position c ^ 2 (r % 4); the swizzle is applied on the
 // source side (each lane fetches the chunk that belongs at its destination).
-// Four stages: while a block is computed, the next three are in flight.  One
-// barrier per iteration: each wave waits for its own fetches of the block
-// (vmcnt), the barrier then publishes the whole stage and frees the stage
-// computed last, which the fetch of block it + 3 refills.
+// Four stages: while a block is computed, the next three are in flight (five
+// measured no faster).  One barrier per iteration: each wave waits for its own
+// fetches of the block (vmcnt), the barrier then publishes the whole stage and
+// frees the stage computed last, which the fetch of block it + 3 refills.
 //
 // Fragments: the transposing LDS read (ds_read_b64_tr_b16) gathers, for a lane,
 // 4 consecutive tokens of one column; two of them form the 8 tokens a lane
@@ -27,8 +28,8 @@
 // kernel's MN-major operand).  With the chunk swizzle above every read phase
 // touches distinct banks (checked by enumeration for 32 and 64 banks).
 //
-// The two k-step halves of each output block are summed in LDS in the fixed
-// order ks = 0, 1 and written once: to the output (one token split) or to the
+// The k-step groups' partials of each output block are summed in LDS in the
+// fixed order ks = 0, 1, ... and written once: to the output (one token split) or to the
 // FP32 workspace plane of the split.  Rows >= N, columns >= K and tokens >= T
 // read as zero (per-lane offsets past the buffer range, and buffer descriptors
 // ending at the last valid token).  Requirements (launcher): 64 < N <= 128,
@@ -40,47 +41,49 @@
 
 namespace dpg {
 
-template <int OUT>
+template <int CB, int OUT>
 __global__ void __launch_bounds__(512, 1) skinny_lds_kernel(SkinnyParams p) {
+  static_assert(CB == 1 || CB == 2, "64-column blocks per unit");
   constexpr int NSTAGE = 4;
-  constexpr int TILE = 64 * 64;       // BF16 elements of one 64-token tile
-  constexpr int STAGE = 4 * TILE;     // X tiles 0, 1 (column blocks), dY tiles 2, 3 (row blocks)
-  constexpr int RED_LD = 68;          // FP32 row stride of the reduction buffer
+  constexpr int TILE = 64 * 64;         // BF16 elements of one 64-token tile
+  constexpr int STAGE = (CB + 2) * TILE;  // X tiles 0 .. CB-1 (column blocks), then 2 dY tiles (row blocks)
+  constexpr int NCH = CB + 2;           // 1 KB fetches per wave per stage (8 waves, 8 per tile)
+  constexpr int KG = 4 / CB;            // k-step groups; a group takes 4 / KG of a block's 4 k-steps
+  constexpr int RED_LD = 68;            // FP32 row stride of the reduction buffer
   constexpr int RED_FLOATS = 8 * 64 * RED_LD;
   constexpr int SMEM_FLOATS = (NSTAGE * STAGE / 2 > RED_FLOATS) ? NSTAGE * STAGE / 2 : RED_FLOATS;
   __shared__ __attribute__((aligned(16))) float smem_f[SMEM_FLOATS];
   __bf16* smem = (__bf16*)smem_f;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int nb = wave & 1, cb = (wave >> 1) & 1, ks = wave >> 2;
+  const int nb = wave & 1, cb = (wave >> 1) % CB, ks = wave / (2 * CB);
 
   const int unit = xcd_remap(blockIdx.x, p.k_blocks * p.splits);
   const int split = unit / p.k_blocks;
   const int kb = unit - split * p.k_blocks;
-  const int c0 = kb * 128;
+  const int c0 = kb * (64 * CB);
   const int tb0 = split * p.tb_per_split;
   const int tb1 = min(tb0 + p.tb_per_split, p.tb_total);
   const int n_iter = max(tb1 - tb0, 0);
 
   const int lddy = (int)p.lddy, ldx = (int)p.ldx;
-  // Fetch assignment: the 32 chunks of 1 KB of a stage, chunk q = 4 w + j of
-  // wave w: tile q / 8 (uniform per wave: waves 0-3 fetch X, 4-7 dY), token
-  // rows 8 (q % 8) .. + 7.  Lane l lands at row 8 (q % 8) + l / 8, chunk
+  // Fetch assignment: the 8 NCH chunks of 1 KB of a stage, chunk q = NCH w + j
+  // of wave w: tile q / 8 (X tiles first, then dY; uniform per wave and j),
+  // token rows 8 (q % 8) .. + 7.  Lane l lands at row 8 (q % 8) + l / 8, chunk
   // position l % 8, and fetches source chunk (l % 8) ^ 2 (row % 4).
-  const bool is_x = wave < 4;
-  const int tile = wave >> 1;
   constexpr uint32_t kOut = 0x80000000u;  // past every buffer range: reads zero
-  uint32_t voff[4];
+  uint32_t voff[NCH];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int q = 4 * wave + j;
+  for (int j = 0; j < NCH; ++j) {
+    const int q = NCH * wave + j;
+    const int tile = q >> 3;
     const int r = 8 * (q & 7) + (lane >> 3);
     const int src = (lane & 7) ^ (2 * (r & 3));
-    if (is_x) {
+    if (tile < CB) {
       const int col = c0 + 64 * tile + 8 * src;
       voff[j] = col < p.K ? (uint32_t)((r * ldx + col) * 2) : kOut;
     } else {
-      const int row = 64 * (tile - 2) + 8 * src;
+      const int row = 64 * (tile - CB) + 8 * src;
       voff[j] = row < p.N ? (uint32_t)((r * lddy + row) * 2) : kOut;
     }
   }
@@ -89,14 +92,18 @@ __global__ void __launch_bounds__(512, 1) skinny_lds_kernel(SkinnyParams p) {
     const bool ok = blk < tb1;
     const int t0 = ok ? blk * 64 : 0;
     const int rows = ok ? min(p.T - t0, 64) : 0;
-    const __bf16* base = is_x ? (const __bf16*)p.x + (int64_t)t0 * ldx : (const __bf16*)p.dy + (int64_t)t0 * lddy;
-    const int bytes = rows > 0 ? ((rows - 1) * (is_x ? ldx : lddy) + (is_x ? p.K : p.N)) * 2 : 0;
-    const rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(base), (short)0, bytes, 0x00020000);
-    __bf16* dst = smem + buf * STAGE + tile * TILE;
+    const int xb = rows > 0 ? ((rows - 1) * ldx + p.K) * 2 : 0;
+    const int yb = rows > 0 ? ((rows - 1) * lddy + p.N) * 2 : 0;
+    const rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>((const __bf16*)p.x + (int64_t)t0 * ldx),
+                                                        (short)0, xb, 0x00020000);
+    const rsrc_t ry = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>((const __bf16*)p.dy + (int64_t)t0 * lddy),
+                                                        (short)0, yb, 0x00020000);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)(dst + ((4 * wave + j) & 7) * 512), 16, (int)voff[j], 0,
-                                               0, 0);
+    for (int j = 0; j < NCH; ++j) {
+      const int q = NCH * wave + j;
+      __bf16* dst = smem + buf * STAGE + (q >> 3) * TILE + (q & 7) * 512;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds((q >> 3) < CB ? rx : ry, (lds_void_t*)dst, 16, (int)voff[j], 0, 0, 0);
+    }
   };
 
   // element (token k, column c) of a tile
@@ -123,20 +130,23 @@ __global__ void __launch_bounds__(512, 1) skinny_lds_kernel(SkinnyParams p) {
   for (int s = 0; s < NSTAGE - 1; ++s) fetch(s, s);
   for (int it = 0; it < n_iter; ++it) {
     // This wave's fetches of block it have landed (those of blocks it + 1 and
-    // it + 2, 8 instructions, may still be in flight; vmcnt counts them in
-    // issue order).  After the barrier every wave's fetches of block it are in
+    // it + 2, 2 (CB + 2) instructions, may still be in flight; vmcnt counts
+    // them in issue order).  After the barrier every wave's fetches of block it are in
     // LDS, and every wave has finished reading the stage of block it - 1 (its
     // reads completed inside their asm blocks), which the fetch below refills.
     // Written out because the compiler would otherwise wait for all fetches
     // here (the release fence of __syncthreads() covers LDS fetches).
-    asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    if constexpr (NCH == 4)
+      asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
     fetch(it + NSTAGE - 1, (it + NSTAGE - 1) % NSTAGE);
     const __bf16* st = smem + (it % NSTAGE) * STAGE;
     const __bf16* xt = st + cb * TILE;
-    const __bf16* yt = st + (2 + nb) * TILE;
+    const __bf16* yt = st + (CB + nb) * TILE;
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int k16 = 2 * ks + s;
+    for (int s = 0; s < 4 / KG; ++s) {
+      const int k16 = (4 / KG) * ks + s;
       // the eight transposing reads of this k-step, complete when the block
       // ends (the compiler would otherwise wait for all in-flight fetches
       // before each read, as it cannot tell the addresses apart)
@@ -186,20 +196,23 @@ __global__ void __launch_bounds__(512, 1) skinny_lds_kernel(SkinnyParams p) {
             f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
       }
   __syncthreads();
-  // output block (nb, cb) = waves nb + 2 cb (ks = 0) and nb + 2 cb + 4 (ks = 1)
+  // output block (nb, cb) = the sum of waves nb + 2 cb + 2 CB ks, ks = 0 .. KG-1 in order
 #pragma unroll
-  for (int hh = 0; hh < 4; ++hh) {
-    const int e = (tid + hh * 512) * 8;         // element index in [4 blocks] x 64 x 64
+  for (int hh = 0; hh < 2 * CB; ++hh) {
+    const int e = (tid + hh * 512) * 8;         // element index in [2 CB blocks] x 64 x 64
     const int blk = e / 4096, rem = e % 4096;   // blk = nb + 2 cb
     const int n = rem / 64, k = rem % 64;
     const float* s0p = smem_f + (blk * 64 + n) * RED_LD + k;
-    const float* s1p = smem_f + ((blk + 4) * 64 + n) * RED_LD + k;
     f32x4 s0 = *(const f32x4*)s0p, s1 = *(const f32x4*)(s0p + 4);
-    const f32x4 a = *(const f32x4*)s1p, b = *(const f32x4*)(s1p + 4);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      s0[r] += a[r];
-      s1[r] += b[r];
+    for (int gg = 1; gg < KG; ++gg) {
+      const float* sp = smem_f + ((blk + 2 * CB * gg) * 64 + n) * RED_LD + k;
+      const f32x4 a = *(const f32x4*)sp, b = *(const f32x4*)(sp + 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        s0[r] += a[r];
+        s1[r] += b[r];
+      }
     }
     const int gn = (blk & 1) * 64 + n, gk = c0 + (blk >> 1) * 64 + k;
     if (gn >= p.N || gk >= p.K) continue;

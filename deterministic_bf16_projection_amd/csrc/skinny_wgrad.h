@@ -5,9 +5,10 @@
 // Work unit = (all N rows, a block of CB * 64 columns of K, token split).  A
 // workgroup has 8 waves arranged as NB row blocks x CB column blocks x TG token
 // groups (NB * CB * TG = 8; NB = 1 for N <= 64, 2 for N <= 128).  The library
-// runs it with CB = 1, i.e. 64-column units, which the planner picks when a
-// small forced split count would leave too few 128-column units; 128-column
-// units run skinny_direct.h (N <= 64) or skinny_lds.h (N <= 128),
+// runs it for N <= 64 with 64-column units (NB = CB = 1), which the planner
+// picks when a small forced split count would leave too few 128-column units;
+// 128-column units run skinny_direct.h (N <= 64), and every unit with two row
+// blocks runs skinny_lds.h,
 // each wave owning a 64 x 64 block of dW.  Per iteration, token group g takes the unit's 64-token
 // block (iteration * TG + g): its X tiles (64 tokens x 64 columns) and dY tiles
 // (64 tokens x 64 rows) are fetched once with 16-byte buffer loads (rows past T

@@ -271,7 +271,8 @@ def test_skinny_wgrad(skinny_x, T, K, N):
 # Exact-integer inputs through the skinny kernels: one and two 64-row blocks of
 # dW with 128-column units (auto plans with enough units: operands straight from
 # registers for one row block, fetched straight into LDS for two) and 64-column
-# units (forced small split counts: the LDS-staged kernel), ragged token tails.
+# units (forced small split counts: the LDS-staged kernel for one row block, the
+# LDS-fetching kernel for two), ragged token tails.
 # (The planner's choices for these shapes are checked on the CPU.)
 SKINNY_EXACT = [
     (4031, 128, 4096),   # two row blocks; 63 token blocks, last holds 63
@@ -307,7 +308,8 @@ def test_skinny_exact_integer(T, N, K):
 # are column slices of wider buffers, dW is written into a column slice of a
 # NaN-filled buffer.  The planner's plans take the register-direct kernel
 # (16400x40x1000), the LDS-fetching kernel (16384x128x4096) and the LDS-staged
-# kernel (4031x64x4096, and every shape with the forced split count of 2).
+# kernel (4031x64x4096, and the N <= 64 shapes with the forced split count of
+# 2; 16384x128x4096 then takes the LDS-fetching kernel's 64-column form).
 @pytest.mark.parametrize("T,N,K", [(16400, 40, 1000), (16384, 128, 4096), (4031, 64, 4096)])
 def test_skinny_padded_strides(T, N, K):
     x, _, dy = dpg_inputs.dense(T, N, K, seed_group=12, kind="int")

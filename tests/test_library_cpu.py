@@ -72,10 +72,10 @@ def test_forced_split_one():
 def test_skinny_unit_shapes():
     """Skinny weight gradients: 128-column units when they give at least half
     as many workgroups as CUs, 64-column units otherwise (forced small split
-    counts); one or two 64-row blocks of dW.  128-column units run the kernels
-    without register staging (one row block: operands straight from registers;
-    two: operands fetched straight into LDS), 64-column units the LDS-staged
-    kernel.  The exact-integer GPU shapes together reach all four variants."""
+    counts); one or two 64-row blocks of dW.  One row block: operands straight
+    from registers (128 columns) or the LDS-staged kernel (64 columns); two row
+    blocks: operands fetched straight into LDS (both widths).  The
+    exact-integer GPU shapes together reach all four variants."""
     def tile(T, N, K, det, split):
         p = plan(2, T, N, K, out=F32, det=det, split=split)
         assert p["kernel"] == "skinny", p
