@@ -306,9 +306,40 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_kernel(GemmParams p) {
 // out[b][m, n] = sum over s = 0, 1, ..., S-1 of ws[b][s][m][n], in that order,
 // then converted to the output type.  Four columns per thread (N % 8 == 0);
 // grid x covers the quads of a row, grid y strides over the rows of all
-// problems.  The loads of eight
-// planes are issued together and then added one after another, so the sum
-// order stays ascending in s.
+// problems.  The loads of up to eight planes are issued together and then
+// added one after another, so the sum order stays ascending in s.
+// v += planes s0, s0 + 1, ..., s0 + R - 1 (in that order) at src; all R loads
+// are issued before the first add
+template <int R>
+__device__ __forceinline__ void add_planes(f32x4& v, const float* src, int s0, int64_t stride) {
+  f32x4 w[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) w[u] = *(const f32x4*)(src + (int64_t)(s0 + u) * stride);
+#pragma unroll
+  for (int u = 0; u < R; ++u) {
+    v[0] += w[u][0];
+    v[1] += w[u][1];
+    v[2] += w[u][2];
+    v[3] += w[u][3];
+  }
+}
+
+// v = plane 0 + plane 1 + ... + plane R-1 (in that order) at src
+template <int R>
+__device__ __forceinline__ void first_planes(f32x4& v, const float* src, int64_t stride) {
+  f32x4 w[R];
+#pragma unroll
+  for (int u = 0; u < R; ++u) w[u] = *(const f32x4*)(src + (int64_t)u * stride);
+  v = w[0];
+#pragma unroll
+  for (int u = 1; u < R; ++u) {
+    v[0] += w[u][0];
+    v[1] += w[u][1];
+    v[2] += w[u][2];
+    v[3] += w[u][3];
+  }
+}
+
 template <int OUT>
 __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restrict__ ws, int S, int64_t split_stride,
                                                             int M, int N, void* out, int64_t ldo, int64_t batch,
@@ -319,26 +350,32 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(const float* __restr
     const int64_t b = mm / M;
     const int m = (int)(mm - b * M);
     const float* src = ws + b * S * split_stride + (int64_t)m * N + n;
-    f32x4 v = *(const f32x4*)src;
-    int s = 1;
-    for (; s + 8 <= S; s += 8) {
-      f32x4 w[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) w[u] = *(const f32x4*)(src + (int64_t)(s + u) * split_stride);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        v[0] += w[u][0];
-        v[1] += w[u][1];
-        v[2] += w[u][2];
-        v[3] += w[u][3];
-      }
+    // planes in batches (the first min(S, 8), then full batches of eight,
+    // then the remainder); every load of a batch is issued before its first
+    // add (a plane-at-a-time loop waits out one memory round trip per plane),
+    // and the adds run in ascending plane order from plane 0
+    f32x4 v;
+    switch (min(S, 8)) {
+      case 8: first_planes<8>(v, src, split_stride); break;
+      case 7: first_planes<7>(v, src, split_stride); break;
+      case 6: first_planes<6>(v, src, split_stride); break;
+      case 5: first_planes<5>(v, src, split_stride); break;
+      case 4: first_planes<4>(v, src, split_stride); break;
+      case 3: first_planes<3>(v, src, split_stride); break;
+      case 2: first_planes<2>(v, src, split_stride); break;
+      default: first_planes<1>(v, src, split_stride); break;
     }
-    for (; s < S; ++s) {
-      const f32x4 w = *(const f32x4*)(src + (int64_t)s * split_stride);
-      v[0] += w[0];
-      v[1] += w[1];
-      v[2] += w[2];
-      v[3] += w[3];
+    int s = min(S, 8);
+    for (; s + 8 <= S; s += 8) add_planes<8>(v, src, s, split_stride);
+    switch (S - s) {
+      case 7: add_planes<7>(v, src, s, split_stride); break;
+      case 6: add_planes<6>(v, src, s, split_stride); break;
+      case 5: add_planes<5>(v, src, s, split_stride); break;
+      case 4: add_planes<4>(v, src, s, split_stride); break;
+      case 3: add_planes<3>(v, src, s, split_stride); break;
+      case 2: add_planes<2>(v, src, s, split_stride); break;
+      case 1: add_planes<1>(v, src, s, split_stride); break;
+      default: break;
     }
     if (OUT == OUT_BF16) {
       u32x2 o = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
