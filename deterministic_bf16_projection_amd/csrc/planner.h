@@ -53,7 +53,7 @@ struct Plan {
   int tile;            // index into kTiles
   int fast;            // software-pipelined kernel (gemm_fast.h) instead of the generic one
   int skinny;          // streaming weight-gradient kernel for N <= 128 (skinny_wgrad.h)
-  int skinny_cols;     // columns of K per skinny work unit (64, 128 or 256)
+  int skinny_cols;     // columns of K per skinny work unit (64 or 128)
   int tiles_m, tiles_n;
   int splits, kt_total, kt_per_split;
   int group_m;
