@@ -65,6 +65,21 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const __bf16* lds_ptr) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// K partition of a split plan: S splits over KB reduction blocks (64
+// elements, or 64 tokens, each); with q = KB / S and r = KB % S the first r
+// splits take q + 1 blocks and the others q, so split s starts at block
+// s q + min(s, r): sizes differ by at most one block, none is empty while
+// S <= KB, and with two splits the first takes ceil(KB / 2) blocks.  q and r
+// come from one division per kernel (split_parts), not one per unit.
+struct SplitParts {
+  int q, r;
+};
+__device__ __forceinline__ SplitParts split_parts(int S, int KB) {
+  const int q = KB / S;
+  return SplitParts{q, KB - q * S};
+}
+__device__ __forceinline__ int split_begin(int s, const SplitParts& sp) { return s * sp.q + min(s, sp.r); }
+
 // Map a linear workgroup id so that the workgroups the dispatcher sends to one
 // XCD (ids congruent mod 8) cover a contiguous range of tile ids.  A bijection
 // on [0, total).

@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <list>
 #include <mutex>
 #include <unordered_map>
 
@@ -21,41 +22,35 @@ namespace dpg {
 namespace {
 
 // ------------------------------------------------------- kernel registry --
-typedef TileCfg<256, 256, 64, 2, 2> TileL;
-typedef TileCfg<128, 128, 64, 2, 2> TileM;
+// The generic kernel is compiled for the 64x64 tile only (the planner's
+// kGenericTile): K tails on K-major operands and row strides beyond 32-bit
+// tile offsets run it; everything else runs the pipelined or skinny kernels.
 typedef TileCfg<64, 64, 64, 2, 2> TileS;
 
 typedef void (*KernelFn)(GemmParams);
 
-template <class Cfg, int LAYOUT, bool X3, int OUT>
-constexpr KernelFn kernel_for() {
-  return &gemm_kernel<Cfg, LAYOUT != LAYOUT_WGRAD, LAYOUT == LAYOUT_FWD, X3, OUT>;
+template <int LAYOUT, bool X3, int OUT>
+constexpr KernelFn generic_for() {
+  return &gemm_kernel<TileS, LAYOUT != LAYOUT_WGRAD, LAYOUT == LAYOUT_FWD, X3, OUT>;
 }
 
-template <class Cfg, int LAYOUT, bool X3>
-struct OutRow {
-  static constexpr KernelFn fns[3] = {X3 ? nullptr : kernel_for<Cfg, LAYOUT, X3, OUT_BF16>(),
-                                      kernel_for<Cfg, LAYOUT, X3, OUT_F32>(),
-                                      kernel_for<Cfg, LAYOUT, X3, OUT_PARTIAL>()};
+template <int LAYOUT, bool X3>
+struct GenericRow {
+  static constexpr KernelFn fns[3] = {X3 ? nullptr : generic_for<LAYOUT, X3, OUT_BF16>(),
+                                      generic_for<LAYOUT, X3, OUT_F32>(), generic_for<LAYOUT, X3, OUT_PARTIAL>()};
 };
 
-// kernel pointer for (tile, layout, x3, out kind); null where not compiled
-KernelFn lookup_kernel(int tile, int layout, int x3, int out_kind) {
-#define DPG_ROW(CFG, L, X)                                              \
-  {OutRow<CFG, L, X>::fns[0], OutRow<CFG, L, X>::fns[1], OutRow<CFG, L, X>::fns[2]}
-  static const KernelFn table[kNumTiles][3][2][3] = {
-      {{DPG_ROW(TileL, 0, false), {nullptr, nullptr, nullptr}},
-       {DPG_ROW(TileL, 1, false), {nullptr, nullptr, nullptr}},
-       {DPG_ROW(TileL, 2, false), {nullptr, nullptr, nullptr}}},
-      {{DPG_ROW(TileM, 0, false), {nullptr, nullptr, nullptr}},
-       {DPG_ROW(TileM, 1, false), {nullptr, nullptr, nullptr}},
-       {DPG_ROW(TileM, 2, false), {nullptr, nullptr, nullptr}}},
-      {{DPG_ROW(TileS, 0, false), DPG_ROW(TileS, 0, true)},
-       {DPG_ROW(TileS, 1, false), DPG_ROW(TileS, 1, true)},
-       {DPG_ROW(TileS, 2, false), DPG_ROW(TileS, 2, true)}},
+// generic 64x64 kernel for (layout, x3, out kind); null where not compiled
+KernelFn lookup_generic_kernel(int layout, int x3, int out_kind) {
+#define DPG_GROW(L, X) {GenericRow<L, X>::fns[0], GenericRow<L, X>::fns[1], GenericRow<L, X>::fns[2]}
+  static const KernelFn table[3][2][3] = {
+      {DPG_GROW(0, false), DPG_GROW(0, true)},
+      {DPG_GROW(1, false), DPG_GROW(1, true)},
+      {DPG_GROW(2, false), DPG_GROW(2, true)},
   };
-#undef DPG_ROW
-  return table[tile][layout][x3][out_kind];
+#undef DPG_GROW
+  if (layout < 0 || layout > 2 || x3 < 0 || x3 > 1 || out_kind < 0 || out_kind > 2) return nullptr;
+  return table[layout][x3][out_kind];
 }
 
 // software-pipelined kernels for the 256x256 and 128x128 tiles (BF16x3: the
@@ -124,8 +119,6 @@ SkinnyFn lookup_skinny_kernel(int nb, int cb, int out_kind) {
   return nullptr;
 }
 
-int tile_threads(int tile) { return kTiles[tile].threads; }
-
 // ----------------------------------------------------------- plan cache --
 struct KeyHash {
   size_t operator()(const PlanKey& k) const {
@@ -141,12 +134,23 @@ struct KeyHash {
     mix((uint64_t)k.cus);
     mix((uint64_t)k.batch);
     mix((uint64_t)k.wlayout);
+    mix((uint64_t)k.generation);
     return (size_t)h;
   }
 };
 
+// Plans cached per key (never a data pointer).  The cache holds at most
+// kCacheCap plans and drops the least recently used one beyond that, so a
+// stream of distinct token counts keeps it bounded.  Keys carry the cache
+// generation that dpg_clear_plan_cache bumps.
+constexpr size_t kCacheCap = 4096;
+struct CacheEntry {
+  PlanKey key;
+  Plan plan;
+};
 std::mutex g_mu;
-std::unordered_map<PlanKey, Plan, KeyHash>* g_cache = nullptr;
+std::list<CacheEntry>* g_lru = nullptr;  // most recently used first
+std::unordered_map<PlanKey, std::list<CacheEntry>::iterator, KeyHash>* g_index = nullptr;
 int64_t g_generation = 0;
 
 // CU count of the current device (fast mode only), cached per device id.
@@ -163,16 +167,27 @@ int device_cus() {
   return cached[dev];
 }
 
-bool get_plan(const PlanKey& key, Plan* plan) {
+bool get_plan(const PlanKey& key_in, Plan* plan) {
   std::lock_guard<std::mutex> lock(g_mu);
-  if (!g_cache) g_cache = new std::unordered_map<PlanKey, Plan, KeyHash>();
-  auto it = g_cache->find(key);
-  if (it != g_cache->end()) {
-    *plan = it->second;
+  if (!g_lru) {
+    g_lru = new std::list<CacheEntry>();
+    g_index = new std::unordered_map<PlanKey, std::list<CacheEntry>::iterator, KeyHash>();
+  }
+  PlanKey key = key_in;
+  key.generation = g_generation;
+  auto it = g_index->find(key);
+  if (it != g_index->end()) {
+    g_lru->splice(g_lru->begin(), *g_lru, it->second);
+    *plan = it->second->plan;
     return true;
   }
   if (!make_plan(key, plan)) return false;
-  g_cache->emplace(key, *plan);
+  g_lru->push_front(CacheEntry{key, *plan});
+  (*g_index)[key] = g_lru->begin();
+  while (g_lru->size() > kCacheCap) {
+    g_index->erase(g_lru->back().key);
+    g_lru->pop_back();
+  }
   return true;
 }
 
@@ -320,9 +335,15 @@ dpg_status run(int pass, int wlayout, int64_t batch, const void* a, int64_t lda,
     return e == hipSuccess ? DPG_OK : DPG_ERR_HIP;
   }
 
-  // the skinny kernel's 64-token tiles span at most 64 * ld * 2 bytes of 32-bit
-  // buffer offsets (below 2^31 for ld < 2^23); larger strides take the generic kernel
-  if (plan.skinny && lda < (1 << 23) && ldb < (1 << 23)) {
+  // The skinny kernels' 64-token tiles span at most 64 * ld * 2 bytes of
+  // 32-bit buffer offsets (below 2^31 for ld < 2^23), the pipelined kernels'
+  // 256-row K-major tiles 256 * ld * 2 bytes (ld < 2^22); wider strides run the
+  // same plan (same K partition and workspace) on the generic kernel.
+  const int64_t ld_max = std::max(lda, ldb);
+  if ((plan.skinny && ld_max >= (1 << 23)) || (!plan.skinny && plan.fast && ld_max >= (1 << 22))) {
+    if (!generic_fallback(&plan)) return DPG_ERR_UNSUPPORTED;
+  }
+  if (plan.skinny) {
     SkinnyParams q;
     q.dy = a;
     q.x = b;
@@ -387,19 +408,16 @@ dpg_status run(int pass, int wlayout, int64_t batch, const void* a, int64_t lda,
     p.batch_c = sc;
     out_kind = out == DPG_BF16 ? OUT_BF16 : OUT_F32;
   }
-  // the pipelined kernel addresses each tile through 32-bit buffer offsets: a
-  // K-major tile of 256 rows spans 256 * ld * 2 bytes, below 2^31 for ld < 2^22
-  const bool ld_ok = lda < (1 << 22) && ldb < (1 << 22);
-  KernelFn fn = (plan.fast && ld_ok) ? lookup_fast_kernel(plan.tile, plan.layout, plan.x3, out_kind)
-                                     : lookup_kernel(plan.tile, plan.layout, plan.x3, out_kind);
+  const bool fast = plan.fast != 0;
+  KernelFn fn = fast ? lookup_fast_kernel(plan.tile, plan.layout, plan.x3, out_kind)
+                     : (plan.tile == kGenericTile ? lookup_generic_kernel(plan.layout, plan.x3, out_kind) : nullptr);
   if (!fn) return DPG_ERR_INVALID_ARG;
   void* args[] = {&p};
-  const bool fast = plan.fast && ld_ok;
-  const int threads = (fast && plan.tile == 0) ? 512 : tile_threads(plan.tile);
+  const int threads = (fast && plan.tile == 0) ? 512 : 256;
   // the pipelined kernel is persistent: one workgroup per CU slot walks its units
-  int64_t grid = plan.skinny ? (int64_t)plan.tiles_m * plan.tiles_n * plan.splits : plan.grid;
-  // (one workgroup per CU for the 256x256 tile and for BF16x3, whose two hi/lo
-  // planes fill the LDS; two for the BF16 128x128 tile)
+  // (one per CU for the 256x256 tile and for BF16x3, whose two hi/lo planes
+  // fill the LDS; two for the BF16 128x128 tile)
+  int64_t grid = plan.grid;
   if (fast) grid = std::min<int64_t>(grid, (int64_t)device_cus() * ((plan.tile == 0 || plan.x3) ? 1 : 2));
   hipError_t e = hipLaunchKernel((const void*)fn, dim3((unsigned)grid), dim3(threads), args, 0, stream);
   if (e != hipSuccess) return DPG_ERR_HIP;
@@ -536,15 +554,20 @@ dpg_status dpg_plan_describe(dpg_pass pass, int64_t T, int64_t N, int64_t K, dpg
 
 void dpg_clear_plan_cache(void) {
   std::lock_guard<std::mutex> lock(g_mu);
-  if (g_cache) g_cache->clear();
+  if (g_lru) {
+    g_index->clear();
+    g_lru->clear();
+  }
   ++g_generation;
 }
 
 void dpg_plan_cache_stats(int64_t* entries, int64_t* generation) {
   std::lock_guard<std::mutex> lock(g_mu);
-  if (entries) *entries = g_cache ? (int64_t)g_cache->size() : 0;
+  if (entries) *entries = g_lru ? (int64_t)g_lru->size() : 0;
   if (generation) *generation = g_generation;
 }
+
+int64_t dpg_plan_cache_capacity(void) { return (int64_t)kCacheCap; }
 
 const char* dpg_status_string(dpg_status status) {
   switch (status) {

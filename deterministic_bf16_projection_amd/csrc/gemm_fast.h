@@ -340,6 +340,7 @@ __device__ __forceinline__ void sched_kstep() {
 struct UnitMap {
   int tiles_m, tiles_n, group_m, splits, kt_per, kt_total, total;
   int per_batch;  // units of one problem (tiles x splits); total = per_batch x problems
+  SplitParts sp;  // K partition of the splits
 };
 
 // Position of a stream of (unit, K tile) steps.
@@ -371,8 +372,8 @@ __device__ __forceinline__ StepCursor cursor_at(const UnitMap& m, int unit) {
   c.row0 = (first_m + r % gsize) * BM;
   c.col0 = (r / gsize) * BN;
   c.split = split;
-  c.kt0 = split * m.kt_per;
-  c.nkt = min(c.kt0 + m.kt_per, m.kt_total) - c.kt0;
+  c.kt0 = split_begin(split, m.sp);
+  c.nkt = split_begin(split + 1, m.sp) - c.kt0;
   return c;
 }
 
@@ -505,7 +506,8 @@ struct FastGemm {
     const InT* B = (const InT*)p.b;
     const int lda = (int)p.lda, ldb = (int)p.ldb;
     const UnitMap um = {p.tiles_m, p.tiles_n, p.group_m, p.splits, p.kt_per_split, p.kt_total,
-                        p.tiles_m * p.tiles_n * p.splits * p.batch, p.tiles_m * p.tiles_n * p.splits};
+                        p.tiles_m * p.tiles_n * p.splits * p.batch, p.tiles_m * p.tiles_n * p.splits,
+                        split_parts(p.splits, p.kt_total)};
     const int stride = gridDim.x;
     OpA opa;
     OpB opb;

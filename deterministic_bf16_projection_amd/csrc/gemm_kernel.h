@@ -33,7 +33,7 @@ struct GemmParams {
   int tiles_m, tiles_n;
   int splits;
   int kt_total;      // ceil(K / BK)
-  int kt_per_split;  // K tiles per split (the last split may hold fewer)
+  int kt_per_split;  // K tiles of the largest split (splits differ by at most one; see split_begin)
   int group_m;       // raster: tiles of one group run down this many tile rows
   int batch;         // independent problems in the launch (units run over all of them)
   int64_t batch_a, batch_b;  // elements between consecutive problems' A and B
@@ -206,8 +206,9 @@ __global__ void __launch_bounds__(Cfg::NT) gemm_kernel(GemmParams p) {
   const int tn = (t % per_group) / gsize;
   const int row0 = tm * BM, col0 = tn * BN;
 
-  const int kt0 = split * p.kt_per_split;
-  const int kt1 = min(kt0 + p.kt_per_split, p.kt_total);
+  const SplitParts sp = split_parts(p.splits, p.kt_total);
+  const int kt0 = split_begin(split, sp);
+  const int kt1 = split_begin(split + 1, sp);
   const int nkt = kt1 - kt0;
 
   const InT* A = (const InT*)p.a + bidx * p.batch_a;

@@ -68,9 +68,9 @@ double estimate_us(const TileShape& ts, bool fast, int64_t batch, int64_t M, int
                    int out_bytes, int in_bytes, int splits_req, int cus, int* splits_out, int* kt_per_out) {
   const int64_t tiles = cdiv(M, ts.bm) * cdiv(N, ts.bn) * batch;
   const int64_t kt_total = cdiv(K, ts.bk);
-  int64_t s = std::min<int64_t>(splits_req, kt_total);
+  // balanced partition: min(request, K tiles) splits, the largest kt_per tiles
+  const int64_t s = std::max<int64_t>(1, std::min<int64_t>(splits_req, kt_total));
   const int64_t kt_per = cdiv(kt_total, s);
-  s = cdiv(kt_total, kt_per);  // no empty splits
   const int64_t units = tiles * s;
   const double flop_unit = 2.0 * ts.bm * ts.bn * (double)(kt_per * ts.bk) * (x3 ? 3 : 1);
   const int64_t occ_used = std::min<int64_t>(x3 ? ts.x3_occupancy : ts.occupancy, cdiv(units, cus));
@@ -137,9 +137,10 @@ bool make_plan(const PlanKey& key, Plan* p) {
       s = (key.cus + units / 2) / units;
       s = std::min<int64_t>(s, std::max<int64_t>(1, p->kt_total / 16));
     }
+    // balanced partition of the 64-token blocks (split_begin in the kernels)
     s = std::max<int64_t>(1, std::min<int64_t>(s, p->kt_total));
+    p->splits = (int)s;
     p->kt_per_split = (int)cdiv(p->kt_total, s);
-    p->splits = (int)cdiv(p->kt_total, p->kt_per_split);
     // 64-column units when 128-column ones would leave more than half the CUs idle
     p->skinny_cols = units * p->splits * 2 >= key.cus ? 128 : 64;
     p->group_m = 1;
@@ -151,37 +152,59 @@ bool make_plan(const PlanKey& key, Plan* p) {
   }
   const int in_bytes = p->x3 ? 4 : 2;
   const int out_bytes = key.out == 1 ? 4 : 2;
+  // the split counts the planner tries on its own; a forced request is
+  // evaluated as it is (any 1..64), on every tile that has a kernel
   static const int kSplitChoices[] = {1, 2, 3, 4, 6, 8, 12, 16, 24, 32, 48, 64};
+  const int forced[1] = {key.split_req};
+  const int* choices = key.split_req > 0 ? forced : kSplitChoices;
+  const int n_choices = key.split_req > 0 ? 1 : (int)(sizeof(kSplitChoices) / sizeof(kSplitChoices[0]));
+  // the pipelined kernels need whole 64-wide K tiles on K-major operands;
+  // without them only the generic 64x64 kernel is compiled
+  const bool kmajor_ok = p->layout == LAYOUT_WGRAD || (p->K % 64) == 0;
   double best = 1e300;
+  int best_tile = -1;
   for (int ti = 0; ti < kNumTiles; ++ti) {
     const TileShape& ts = kTiles[ti];
+    const bool fast = ts.fast_ok && kmajor_ok;
+    if (!fast && ti != kGenericTile) continue;
     if (p->x3 && !ts.x3_ok) continue;
-    for (int sc : kSplitChoices) {
-      if (key.split_req != 0 && sc != key.split_req) continue;
+    for (int c = 0; c < n_choices; ++c) {
       int s, ktp;
-      const bool fast = ts.fast_ok && (p->layout == LAYOUT_WGRAD || p->K % 64 == 0);
-      const double t =
-          estimate_us(ts, fast, p->batch, p->M, p->N, p->K, p->x3, out_bytes, in_bytes, sc, key.cus, &s, &ktp);
-      if (t < best * 0.97) {  // prefer the earlier (larger tile, fewer splits) choice unless 3% faster
+      const double t = estimate_us(ts, fast, p->batch, p->M, p->N, p->K, p->x3, out_bytes, in_bytes, choices[c],
+                                   key.cus, &s, &ktp);
+      if (best_tile < 0 || t < best * 0.97) {  // prefer the earlier (larger tile, fewer splits) unless 3% faster
         best = t;
-        p->tile = ti;
+        best_tile = ti;
         p->splits = s;
         p->kt_per_split = ktp;
       }
     }
-    if (key.split_req != 0 && key.split_req > 64) return false;
   }
+  if (best_tile < 0) return false;
+  p->tile = best_tile;
   const TileShape& ts = kTiles[p->tile];
   p->tiles_m = (int)cdiv(p->M, ts.bm);
   p->tiles_n = (int)cdiv(p->N, ts.bn);
   p->kt_total = (int)cdiv(p->K, ts.bk);
   p->group_m = std::min(p->tiles_m, 8);
-  // the pipelined kernel needs whole 64-wide K tiles on K-major operands
-  const bool kmajor_ok = p->layout == LAYOUT_WGRAD || (p->K % 64) == 0;
   p->fast = (ts.fast_ok && kmajor_ok) ? 1 : 0;
   p->grid = (int64_t)p->tiles_m * p->tiles_n * p->splits * p->batch;
   p->ws_bytes = p->splits > 1 ? (size_t)p->batch * p->splits * (size_t)p->M * (size_t)p->N * 4u : 0;
   p->est_us = best;
+  return p->grid <= INT32_MAX;
+}
+
+bool generic_fallback(Plan* p) {
+  if (p->kind != PLAN_GEMM) return true;
+  const TileShape& ts = kTiles[kGenericTile];
+  p->tile = kGenericTile;
+  p->fast = 0;
+  p->skinny = 0;
+  p->skinny_cols = 0;
+  p->tiles_m = (int)cdiv(p->M, ts.bm);
+  p->tiles_n = (int)cdiv(p->N, ts.bn);
+  p->group_m = std::min(p->tiles_m, 8);
+  p->grid = (int64_t)p->tiles_m * p->tiles_n * p->splits * p->batch;
   return p->grid <= INT32_MAX;
 }
 

@@ -23,6 +23,7 @@ struct TileShape {
   bool fast_ok;    // a software-pipelined variant exists for this tile
 };
 constexpr int kNumTiles = 3;
+constexpr int kGenericTile = 2;  // the only tile with a generic (non-pipelined) kernel
 extern const TileShape kTiles[kNumTiles];
 
 enum WeightLayout { WEIGHT_NK = 0, WEIGHT_KN = 1 };
@@ -36,9 +37,11 @@ struct PlanKey {
   int cus;         // CU count the plan was made for (fixed 256 in deterministic mode)
   int64_t batch = 1;         // independent problems of the same shape in one launch
   int wlayout = WEIGHT_NK;   // weight (or weight-gradient) stored [N,K] or [K,N]
+  int64_t generation = 0;    // plan-cache generation (the planner ignores it)
   bool operator==(const PlanKey& o) const {
     return pass == o.pass && T == o.T && N == o.N && K == o.K && out == o.out && det == o.det &&
-           split_req == o.split_req && cus == o.cus && batch == o.batch && wlayout == o.wlayout;
+           split_req == o.split_req && cus == o.cus && batch == o.batch && wlayout == o.wlayout &&
+           generation == o.generation;
   }
 };
 
@@ -66,7 +69,21 @@ struct Plan {
 constexpr int kDetCus = 256;
 
 // Builds the plan for a key; returns false for arguments no plan covers.
+// A GEMM plan of S > 1 splits partitions the kt_total K tiles (64 elements, or
+// 64 tokens for a weight gradient) evenly: with q = kt_total / S and r =
+// kt_total % S, the first r splits take q + 1 tiles and the rest q (split s
+// starts at tile s q + min(s, r)); kt_per_split is the largest split.  A forced split
+// count is min(split_req, kt_total).  Every plan names a kernel that exists:
+// the pipelined kernels (256x256, 128x128, and BF16x3 on 128x128) need whole
+// K tiles on K-major operands, otherwise the generic 64x64 kernel runs.
 bool make_plan(const PlanKey& key, Plan* plan);
+
+// Moves a GEMM plan onto the generic 64x64 kernel (64-bit addressing), for
+// calls whose row strides are beyond the pipelined and skinny kernels' 32-bit
+// tile offsets.  The K partition, hence the workspace size and (for one MFMA
+// instruction and k order) the output bits, stays the same.  Returns false if
+// the launch would exceed the grid limit.
+bool generic_fallback(Plan* plan);
 
 // One-line description of a plan.
 int describe_plan(const PlanKey& key, const Plan& plan, char* buf, size_t buflen);

@@ -50,8 +50,9 @@ __global__ void __launch_bounds__(512, 1) skinny_direct_kernel(SkinnyParams p) {
   const int split = unit / p.k_blocks;
   const int kb = unit - split * p.k_blocks;
   const int c0 = kb * COLS;
-  const int tb0 = split * p.tb_per_split;
-  const int tb1 = min(tb0 + p.tb_per_split, p.tb_total);
+  const SplitParts sp = split_parts(p.splits, p.tb_total);
+  const int tb0 = split_begin(split, sp);
+  const int tb1 = split_begin(split + 1, sp);
   const int steps = max(tb1 - tb0, 0) * 4;          // 16-token steps of the unit
   const int n_my = steps > wave ? (steps - wave + W - 1) / W : 0;
 

@@ -62,8 +62,9 @@ __global__ void __launch_bounds__(512, 1) skinny_lds_kernel(SkinnyParams p) {
   const int split = unit / p.k_blocks;
   const int kb = unit - split * p.k_blocks;
   const int c0 = kb * (64 * CB);
-  const int tb0 = split * p.tb_per_split;
-  const int tb1 = min(tb0 + p.tb_per_split, p.tb_total);
+  const SplitParts sp = split_parts(p.splits, p.tb_total);
+  const int tb0 = split_begin(split, sp);
+  const int tb1 = split_begin(split + 1, sp);
   const int n_iter = max(tb1 - tb0, 0);
 
   const int lddy = (int)p.lddy, ldx = (int)p.ldx;

@@ -32,7 +32,7 @@ struct SkinnyParams {
   int64_t split_stride;  // elements between workspace planes
   int T, N, K;
   int k_blocks, splits;        // column blocks of K (CB * 64 columns); token splits
-  int tb_total, tb_per_split;  // 64-token blocks and blocks per split
+  int tb_total, tb_per_split;  // 64-token blocks; blocks of the largest split (see split_begin)
 };
 
 template <int NB, int CB, int OUT>
@@ -60,8 +60,9 @@ __global__ void __launch_bounds__(512, 1) skinny_wgrad_kernel(SkinnyParams p) {
   const int split = unit / p.k_blocks;
   const int kb = unit - split * p.k_blocks;
   const int c0 = kb * (CB * 64);
-  const int tb0 = split * p.tb_per_split;
-  const int tb1 = min(tb0 + p.tb_per_split, p.tb_total);
+  const SplitParts sp = split_parts(p.splits, p.tb_total);
+  const int tb0 = split_begin(split, sp);
+  const int tb1 = split_begin(split + 1, sp);
   const int n_iter = (tb1 - tb0 + TG - 1) / TG;
 
   const __bf16* dy = (const __bf16*)p.dy;

@@ -40,7 +40,13 @@
  *   the device, its CU count or the cache state -- so the bits are reproducible
  *   on any MI355X.  deterministic == 0 selects the split-K plan, which may also
  *   use the device's CU count to pick the K split.  `split_k` = 0 lets the
- *   planner choose; 1..64 forces that many K splits in either mode.  In BOTH
+ *   planner choose; 1..64 forces min(split_k, B) K splits in either mode, B
+ *   being the number of 64-element blocks of the reduction (K for the forward
+ *   pass, N for the input gradient, 64-token blocks of T for the weight
+ *   gradient).  S splits partition the blocks evenly: with q = B / S and
+ *   r = B % S the first r splits take q + 1 blocks and the others q (split s
+ *   starts at block s*q + min(s, r); for S = 2: [0, ceil(B/2)) and the rest).
+ *   In BOTH
  *   modes every reduction runs in a fixed order with no atomics, so repeated
  *   calls with the same arguments on one device give bitwise-identical
  *   outputs; different plans may differ from each other in the last bits.
@@ -66,7 +72,7 @@ extern "C" {
 typedef enum {
   DPG_OK = 0,
   DPG_ERR_INVALID_ARG = 1, /* negative size, ld < cols, NULL pointer for non-empty data, bad enum */
-  DPG_ERR_UNSUPPORTED = 2, /* split_k outside 0..64 */
+  DPG_ERR_UNSUPPORTED = 2, /* split_k outside 0..64, or a launch beyond the grid limit */
   DPG_ERR_ALIGNMENT = 3,   /* pointer / ld / contiguous extent not 16-byte compatible */
   DPG_ERR_WORKSPACE = 4,   /* workspace smaller than dpg_workspace_size() */
   DPG_ERR_HIP = 5          /* a kernel launch failed */
@@ -74,13 +80,20 @@ typedef enum {
 
 typedef enum { DPG_BF16 = 0, DPG_F32 = 1 } dpg_dtype;
 
+/* Passes; the short names (DPG_FWD ...) are aliases of the long ones. */
 typedef enum {
   DPG_PASS_FORWARD = 0,
   DPG_PASS_DGRAD = 1,
   DPG_PASS_WGRAD = 2,
   DPG_PASS_ROUTER_FORWARD = 3,
   DPG_PASS_ROUTER_DGRAD = 4,
-  DPG_PASS_ROUTER_WGRAD = 5
+  DPG_PASS_ROUTER_WGRAD = 5,
+  DPG_FWD = DPG_PASS_FORWARD,
+  DPG_DGRAD = DPG_PASS_DGRAD,
+  DPG_WGRAD = DPG_PASS_WGRAD,
+  DPG_ROUTER_FWD = DPG_PASS_ROUTER_FORWARD,
+  DPG_ROUTER_DGRAD = DPG_PASS_ROUTER_DGRAD,
+  DPG_ROUTER_WGRAD = DPG_PASS_ROUTER_WGRAD
 } dpg_pass;
 
 /*
@@ -200,8 +213,13 @@ dpg_status dpg_plan_describe_batched(dpg_pass pass, dpg_weight_layout w_layout, 
 
 /*
  * Bytes of workspace the call with these arguments needs (0 when the plan has a
- * single K split).  For router passes N = E, K = H and out_dtype must be DPG_F32.
- * Returns (size_t)-1 for arguments the matching call would reject.
+ * single K split): the FP32 partial products of the splits, S planes of the
+ * output's rows x columns, which a second kernel adds in ascending split order
+ * (the router page's commit message sums the split partials positionally over
+ * the split dimension; the K1 weight-gradient page's description names one and
+ * two K splits).  For router passes N = E, K = H and out_dtype must be DPG_F32.
+ * Returns (size_t)-1 for arguments the matching call would reject.  The size
+ * does not depend on the row strides.
  */
 size_t dpg_workspace_size(dpg_pass pass, int64_t T, int64_t N, int64_t K, dpg_dtype out_dtype,
                           int deterministic, int split_k);
@@ -209,22 +227,36 @@ size_t dpg_workspace_size(dpg_pass pass, int64_t T, int64_t N, int64_t K, dpg_dt
 /*
  * Host-only description of the plan the library would use (kernel variant,
  * tile, raster group, K splits and their K-block partition, workspace) as one
- * line of text in `buf` (truncated to buflen - 1 characters, NUL-terminated).
- * Makes no HIP call; usable without a GPU.
+ * line of text in `buf` (truncated to buflen - 1 characters, NUL-terminated):
+ * the plan a key maps to, as the row-half-release page's description keys its
+ * programs by exact token count and the router page's commit message keys
+ * entries by shape, split count and alignment.  Split-K mode is described for
+ * 256 CUs.  Row strides of 2^22 elements or more run the same K partition on
+ * the generic kernel, which this text does not show.  Makes no HIP call;
+ * usable without a GPU.  DPG_ERR_INVALID_ARG for a NULL or empty buffer or
+ * arguments no plan covers.
  */
 dpg_status dpg_plan_describe(dpg_pass pass, int64_t T, int64_t N, int64_t K, dpg_dtype out_dtype,
                              int deterministic, int split_k, char* buf, size_t buflen);
 
-/* Drops every cached plan and bumps the cache generation.  Thread-safe. */
+/*
+ * The plan cache (router page, commit message and review: calls are cached by
+ * their own arguments, never by data pointers, and the cache is refreshed when
+ * the route changes).  It is process-global and mutex-protected, holds at most
+ * dpg_plan_cache_capacity() plans (least recently used out first), and its
+ * keys carry a generation number.  dpg_clear_plan_cache drops every plan and
+ * bumps the generation; it never fails.  dpg_plan_cache_stats writes the
+ * number of cached plans and the generation through the non-NULL pointers.
+ */
 void dpg_clear_plan_cache(void);
-
-/* Number of plans in the cache and the current cache generation (host-only). */
 void dpg_plan_cache_stats(int64_t* entries, int64_t* generation);
+int64_t dpg_plan_cache_capacity(void);
 
-/* Static text for a status code. */
+/* Static text for a status code ("unknown status" for other values); the
+ * error classes follow the validation rules above. */
 const char* dpg_status_string(dpg_status status);
 
-/* Library version string. */
+/* Library version string (static text naming the target, gfx950). */
 const char* dpg_version(void);
 
 #ifdef __cplusplus

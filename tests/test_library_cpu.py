@@ -119,6 +119,104 @@ def test_medium_projection_plans():
     assert pick(2, 512) == ("256x256x64", "8")
 
 
+# shapes of every workload (T, N, K as the entry points take them) plus K tails
+FORCED_SPLIT_SHAPES = [
+    (64, 1024, 4096), (16384, 12288, 4096), (16231, 12288, 4096), (16384, 64, 4096), (65537, 128, 4096),
+    (1025, 48, 5120), (4031, 64, 5120), (16384, 512, 4096), (333, 200, 264), (1, 8, 8), (4096, 4104, 1032),
+]
+ROUTER_SHAPES = [(64, 256, 4096), (256, 256, 4096), (1024, 256, 4096), (4096, 256, 4104), (96, 256, 1024)]
+
+
+def _reduction_blocks(pass_, T, N, K):
+    return -(-{0: K, 1: N, 2: T}[pass_ % 3] // 64)
+
+
+def _check_plan(pass_, T, N, K, out, det, split):
+    p = plan(pass_, T, N, K, out=out, det=det, split=split)
+    assert p["kind"] == "gemm", p
+    blocks = _reduction_blocks(pass_, T, N, K)
+    assert int(p["kt_total"]) == blocks
+    s = int(p["splits"])
+    assert s == (min(split, blocks) if split else s) and 1 <= s <= blocks, (split, p)
+    assert int(p["kt_per_split"]) == -(-blocks // s)
+    assert int(p["grid"]) >= 1
+    # every plan names a compiled kernel: pipelined 256x256 / 128x128 (BF16x3 on
+    # 128x128 only), the skinny kernels, or the generic kernel on 64x64 tiles
+    kernel, tile = p["kernel"], p["tile"]
+    assert kernel in ("pipelined", "generic", "skinny"), p
+    if kernel == "generic":
+        assert tile == "64x64x64", p
+    if kernel == "pipelined":
+        assert tile in ("256x256x64", "128x128x64"), p
+        assert p["x3"] == "0" or tile == "128x128x64", p
+    M, Nn = int(p["M"]), int(p["N"])
+    assert int(p["workspace"]) == (s * M * Nn * 4 if s > 1 else 0), p
+    assert L.dpg_workspace_size(pass_, T, N, K, out, det, split) == int(p["workspace"])
+    return p
+
+
+@pytest.mark.parametrize("split", range(0, 65))
+def test_forced_split_counts_all_passes(split):
+    """Any split_k in 1..64 gives min(split_k, B) splits of the balanced
+    partition (B = 64-element blocks of the reduction) on a compiled kernel,
+    with the workspace sized for exactly those splits, for every pass."""
+    for T, N, K in FORCED_SPLIT_SHAPES:
+        for pass_ in (0, 1, 2):
+            for out in (BF16, F32):
+                for det in (1, 0):
+                    _check_plan(pass_, T, N, K, out, det, split)
+    for T, E, H in ROUTER_SHAPES:
+        for pass_ in (3, 4, 5):
+            for det in (1, 0):
+                p = _check_plan(pass_, T, E, H, F32, det, split)
+                assert p["x3"] == "1"
+
+
+def test_k_tails_take_the_generic_64_tile():
+    """A K-major reduction that is not a multiple of 64 has no pipelined
+    kernel: the plan is the generic kernel on 64x64 tiles (the 256x256 and
+    128x128 generic variants are not compiled), whatever the split."""
+    for pass_, T, N, K in [(0, 16384, 12288, 4104), (0, 4096, 4096, 1032), (1, 4096, 1032, 4096),
+                           (1, 16384, 4104, 12288), (3, 4096, 256, 4104)]:
+        for split in (0, 1, 2, 5):
+            p = plan(pass_, T, N, K, out=F32, det=1, split=split)
+            assert p["kernel"] == "generic" and p["tile"] == "64x64x64", p
+    # the weight gradient's operands are MN-major: ragged T stays pipelined
+    p = plan(2, 16231, 12288, 4096)
+    assert p["kernel"] == "pipelined", p
+
+
+def test_balanced_partition_sizes():
+    """Forced split counts that do not divide the block count: sizes differ by
+    at most one block and none is empty (63 splits of 64 blocks: 62 of one
+    block and one of two, not 32 splits of two)."""
+    p = plan(0, 1024, 1024, 4096, det=0, split=63)
+    assert p["splits"] == "63" and p["kt_per_split"] == "2", p
+    p = plan(0, 1024, 1024, 4096, det=0, split=5)
+    assert p["splits"] == "5" and p["kt_per_split"] == "13", p
+    p = plan(2, 16384, 64, 4096, out=F32, det=0, split=7)
+    assert p["kernel"] == "skinny" and p["splits"] == "7" and p["kt_per_split"] == "37", p
+
+
+def test_plan_cache_bounded():
+    """10k distinct token counts keep the cache at its capacity (least
+    recently used plans dropped); a cleared cache starts a new generation."""
+    dpg.clear_plan_cache()
+    cap = dpg.plan_cache_capacity()
+    assert 0 < cap <= 100000
+    for T in range(1, 10001):
+        assert L.dpg_workspace_size(2, T, 64, 4096, F32, 1, 0) != ctypes.c_size_t(-1).value
+    e, g = dpg.plan_cache_stats()
+    assert e == min(cap, 10000)
+    # a recently used key stays cached while older ones are dropped
+    L.dpg_workspace_size(2, 10000, 64, 4096, F32, 1, 0)
+    e2, g2 = dpg.plan_cache_stats()
+    assert e2 == e and g2 == g
+    dpg.clear_plan_cache()
+    e3, g3 = dpg.plan_cache_stats()
+    assert e3 == 0 and g3 == g + 1
+
+
 def test_router_uses_bf16x3():
     p = plan(3, 64, 256, 4096, out=F32)
     assert p["x3"] == "1"
@@ -183,6 +281,12 @@ def test_validation_errors():
     assert fwd(out=7) == 1                        # bad dtype
     assert fwd(split=65) == 2
     assert fwd(split=-1) == 2
+    # forced split counts outside the old list are planned, not rejected:
+    # without a workspace the call stops at the workspace check (no launch)
+    for split in (5, 7, 63):
+        assert L.dpg_wgrad(FAKE, 64, FAKE, 64, FAKE, 64, F32, 4096, 64, 64, 0, split, None, 0, None) == 4
+        assert L.dpg_router_forward(FAKE, 4096, FAKE, 4096, FAKE, 256, 64, 256, 4096, 1, split, None, 0,
+                                    None) == 4
     # a forced split needs a workspace
     assert L.dpg_wgrad(FAKE, 64, FAKE, 64, FAKE, 64, F32, 4096, 64, 64, 0, 2, None, 0, None) == 4
     assert L.dpg_router_forward(FAKE, 64, FAKE + 4, 64, FAKE, 64, 16, 64, 64, 1, 0, None, 0, None) == 3
