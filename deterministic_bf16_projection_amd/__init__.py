@@ -11,6 +11,7 @@ Names follow the C ABI: ``dpg_forward``, ``dpg_dgrad``, ``dpg_wgrad``,
 batched ``dpg_forward_batched``, ``dpg_dgrad_batched``, ``dpg_wgrad_batched``.
 ``deterministic=True`` is the default, as on the router page's description.
 """
+import contextlib
 import ctypes
 import os
 import re
@@ -61,6 +62,8 @@ _lib.dpg_clear_plan_cache.argtypes = []
 _lib.dpg_clear_plan_cache.restype = None
 _lib.dpg_plan_cache_stats.argtypes = [ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
 _lib.dpg_plan_cache_stats.restype = None
+_lib.dpg_plan_cache_capacity.argtypes = []
+_lib.dpg_plan_cache_capacity.restype = _i64
 _lib.dpg_status_string.argtypes = [_ci]
 _lib.dpg_status_string.restype = ctypes.c_char_p
 _lib.dpg_version.argtypes = []
@@ -118,6 +121,19 @@ def _stream(stream):
     return int(stream)
 
 
+def _on_stream(stream, device):
+    """Context in which the binding allocates the tensors a call creates (its
+    output and workspace): the stream the kernels run on.  PyTorch's caching
+    allocator then reuses such a block only after that stream's work on it, so
+    a workspace dropped when the call returns cannot be handed to other work
+    while the kernels still read it."""
+    if stream is None:
+        return contextlib.nullcontext()
+    if not isinstance(stream, torch.cuda.Stream):
+        stream = torch.cuda.ExternalStream(int(stream), device=device)
+    return torch.cuda.stream(stream)
+
+
 def workspace_size(pass_, T, N, K, out_dtype=torch.bfloat16, deterministic=True, split_k=0):
     n = _lib.dpg_workspace_size(pass_, T, N, K, _code(out_dtype), int(bool(deterministic)), split_k)
     if n == ctypes.c_size_t(-1).value:
@@ -148,6 +164,10 @@ def plan_cache_stats():
     return e.value, g.value
 
 
+def plan_cache_capacity():
+    return _lib.dpg_plan_cache_capacity()
+
+
 def _workspace(pass_, T, N, K, out_code, det, split_k, workspace, device):
     need = _lib.dpg_workspace_size(pass_, T, N, K, out_code, det, split_k)
     if need == ctypes.c_size_t(-1).value:
@@ -164,7 +184,8 @@ def _workspace(pass_, T, N, K, out_code, det, split_k, workspace, device):
 
 def _call(name, pass_, a, b, out, out_code, T, N, K, deterministic, split_k, workspace, stream):
     det = int(bool(deterministic))
-    ws, ws_bytes = _workspace(pass_, T, N, K, out_code, det, split_k, workspace, out.device)
+    with _on_stream(stream, out.device):
+        ws, ws_bytes = _workspace(pass_, T, N, K, out_code, det, split_k, workspace, out.device)
     fn = getattr(_lib, name)
     args = [a.data_ptr(), _ld(a, "a"), b.data_ptr(), _ld(b, "b"), out.data_ptr(), _ld(out, "out")]
     if pass_ < 3:
@@ -218,7 +239,8 @@ def dpg_forward(x, w, out=None, out_dtype=torch.bfloat16, deterministic=True, sp
         raise ValueError("w must be [N, K]")
     _check_same_device(("x", x), ("w", w))
     if out is None:
-        out = torch.empty((T, N), dtype=out_dtype, device=x.device)
+        with _on_stream(stream, x.device):
+            out = torch.empty((T, N), dtype=out_dtype, device=x.device)
     _check_out(out, (T, N), x.device)
     return _call("dpg_forward", PASS_FORWARD, x, w, out, _code(out.dtype), T, N, K, deterministic, split_k,
                  workspace, stream)
@@ -235,7 +257,8 @@ def dpg_dgrad(dy, w, out=None, out_dtype=torch.bfloat16, deterministic=True, spl
         raise ValueError("w must be [N, K]")
     _check_same_device(("dy", dy), ("w", w))
     if out is None:
-        out = torch.empty((T, K), dtype=out_dtype, device=dy.device)
+        with _on_stream(stream, dy.device):
+            out = torch.empty((T, K), dtype=out_dtype, device=dy.device)
     _check_out(out, (T, K), dy.device)
     return _call("dpg_dgrad", PASS_DGRAD, dy, w, out, _code(out.dtype), T, N, K, deterministic, split_k,
                  workspace, stream)
@@ -252,7 +275,8 @@ def dpg_wgrad(dy, x, out=None, out_dtype=torch.bfloat16, deterministic=True, spl
         raise ValueError("x must be [T, K]")
     _check_same_device(("dy", dy), ("x", x))
     if out is None:
-        out = torch.empty((N, K), dtype=out_dtype, device=dy.device)
+        with _on_stream(stream, dy.device):
+            out = torch.empty((N, K), dtype=out_dtype, device=dy.device)
     _check_out(out, (N, K), dy.device)
     return _call("dpg_wgrad", PASS_WGRAD, dy, x, out, _code(out.dtype), T, N, K, deterministic, split_k,
                  workspace, stream)
@@ -268,7 +292,8 @@ def dpg_router_forward(x, w, out=None, deterministic=True, split_k=0, workspace=
         raise ValueError("w must be [E, H]")
     _check_same_device(("x", x), ("w", w))
     if out is None:
-        out = torch.empty((T, E), dtype=torch.float32, device=x.device)
+        with _on_stream(stream, x.device):
+            out = torch.empty((T, E), dtype=torch.float32, device=x.device)
     _check_in(out, torch.float32, "out")
     _check_out(out, (T, E), x.device)
     return _call("dpg_router_forward", PASS_ROUTER_FORWARD, x, w, out, F32, T, E, H, deterministic, split_k,
@@ -285,7 +310,8 @@ def dpg_router_dgrad(dy, w, out=None, deterministic=True, split_k=0, workspace=N
         raise ValueError("w must be [E, H]")
     _check_same_device(("dy", dy), ("w", w))
     if out is None:
-        out = torch.empty((T, H), dtype=torch.float32, device=dy.device)
+        with _on_stream(stream, dy.device):
+            out = torch.empty((T, H), dtype=torch.float32, device=dy.device)
     _check_in(out, torch.float32, "out")
     _check_out(out, (T, H), dy.device)
     return _call("dpg_router_dgrad", PASS_ROUTER_DGRAD, dy, w, out, F32, T, E, H, deterministic, split_k,
@@ -302,7 +328,8 @@ def dpg_router_wgrad(dy, x, out=None, deterministic=True, split_k=0, workspace=N
         raise ValueError("x must be [T, H]")
     _check_same_device(("dy", dy), ("x", x))
     if out is None:
-        out = torch.empty((E, H), dtype=torch.float32, device=dy.device)
+        with _on_stream(stream, dy.device):
+            out = torch.empty((E, H), dtype=torch.float32, device=dy.device)
     _check_in(out, torch.float32, "out")
     _check_out(out, (E, H), dy.device)
     return _call("dpg_router_wgrad", PASS_ROUTER_WGRAD, dy, x, out, F32, T, E, H, deterministic, split_k,
@@ -385,13 +412,15 @@ def dpg_forward_batched(x, w, out=None, out_dtype=torch.bfloat16, weight_layout=
         raise ValueError("weight does not match K")
     _check_same_device(("x", x), ("w", w))
     if out is None:
-        out = torch.empty((batch, T, N), dtype=out_dtype, device=x.device)
+        with _on_stream(stream, x.device):
+            out = torch.empty((batch, T, N), dtype=out_dtype, device=x.device)
     _check_out(out, (batch, T, N), x.device)
     x3, sx, ldx = _batched(x, "x", batch)
     w3, sw, ldw = _batched(w, "w", batch)
     o3, so, ldo = _batched(out, "out", batch)
     det = int(bool(deterministic))
-    ws, wsb = _batched_ws(PASS_FORWARD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace, x.device)
+    with _on_stream(stream, x.device):
+        ws, wsb = _batched_ws(PASS_FORWARD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace, x.device)
     st = _lib.dpg_forward_batched(x3.data_ptr(), ldx, sx, w3.data_ptr(), ldw, sw, wl, o3.data_ptr(), ldo, so,
                                   _code(out.dtype), batch, T, N, K, det, split_k,
                                   ws.data_ptr() if ws is not None else None, wsb, _stream(stream))
@@ -413,13 +442,15 @@ def dpg_dgrad_batched(dy, w, out=None, out_dtype=torch.bfloat16, weight_layout="
         raise ValueError("weight does not match N")
     _check_same_device(("dy", dy), ("w", w))
     if out is None:
-        out = torch.empty((batch, T, K), dtype=out_dtype, device=dy.device)
+        with _on_stream(stream, dy.device):
+            out = torch.empty((batch, T, K), dtype=out_dtype, device=dy.device)
     _check_out(out, (batch, T, K), dy.device)
     d3, sd, ldd = _batched(dy, "dy", batch)
     w3, sw, ldw = _batched(w, "w", batch)
     o3, so, ldo = _batched(out, "out", batch)
     det = int(bool(deterministic))
-    ws, wsb = _batched_ws(PASS_DGRAD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace, dy.device)
+    with _on_stream(stream, dy.device):
+        ws, wsb = _batched_ws(PASS_DGRAD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace, dy.device)
     st = _lib.dpg_dgrad_batched(d3.data_ptr(), ldd, sd, w3.data_ptr(), ldw, sw, wl, o3.data_ptr(), ldo, so,
                                 _code(out.dtype), batch, T, N, K, det, split_k,
                                 ws.data_ptr() if ws is not None else None, wsb, _stream(stream))
@@ -442,13 +473,15 @@ def dpg_wgrad_batched(dy, x, out=None, out_dtype=torch.bfloat16, weight_layout="
     _check_same_device(("dy", dy), ("x", x))
     oshape = (batch, N, K) if wl == 0 else (batch, K, N)
     if out is None:
-        out = torch.empty(oshape, dtype=out_dtype, device=dy.device)
+        with _on_stream(stream, dy.device):
+            out = torch.empty(oshape, dtype=out_dtype, device=dy.device)
     _check_out(out, oshape, dy.device)
     d3, sd, ldd = _batched(dy, "dy", batch)
     x3, sx, ldx = _batched(x, "x", batch)
     o3, so, ldo = _batched(out, "out", batch)
     det = int(bool(deterministic))
-    ws, wsb = _batched_ws(PASS_WGRAD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace, dy.device)
+    with _on_stream(stream, dy.device):
+        ws, wsb = _batched_ws(PASS_WGRAD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace, dy.device)
     st = _lib.dpg_wgrad_batched(d3.data_ptr(), ldd, sd, x3.data_ptr(), ldx, sx, o3.data_ptr(), ldo, so, wl,
                                 _code(out.dtype), batch, T, N, K, det, split_k,
                                 ws.data_ptr() if ws is not None else None, wsb, _stream(stream))

@@ -45,26 +45,32 @@ def _rows(t):
 
 class _Projection(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, w, deterministic, out_dtype):
+    def forward(ctx, x, w, deterministic, out_dtype, round_grad):
         x2 = _rows(x)
         y = dpg_forward(x2, w, out_dtype=out_dtype, deterministic=deterministic)
         ctx.save_for_backward(x2, w)
         ctx.deterministic = deterministic
+        ctx.round_grad = round_grad
         ctx.x_shape = x.shape
         return y.reshape(*x.shape[:-1], w.shape[0])
 
     @staticmethod
     def backward(ctx, dy):
         x2, w = ctx.saved_tensors
-        # the library's gradient passes take BF16 dY (an FP32 forward output
-        # gets a BF16-rounded gradient)
-        dy2 = _rows(dy if dy.dtype == torch.bfloat16 else dy.to(torch.bfloat16))
+        # the library's gradient passes take a BF16 dY; any other incoming
+        # gradient is rounded (nearest even) only when the caller asked for it
+        if dy.dtype != torch.bfloat16:
+            if not ctx.round_grad:
+                raise TypeError("projection: the incoming gradient is %s, but the gradient GEMMs take BF16; "
+                                "pass round_grad_to_bf16=True to round it to BF16 explicitly" % dy.dtype)
+            dy = dy.to(torch.bfloat16)
+        dy2 = _rows(dy)
         dx = dw = None
         if ctx.needs_input_grad[0]:
             dx = dpg_dgrad(dy2, w, out_dtype=torch.bfloat16, deterministic=ctx.deterministic).reshape(ctx.x_shape)
         if ctx.needs_input_grad[1]:
             dw = dpg_wgrad(dy2, x2, out_dtype=torch.bfloat16, deterministic=ctx.deterministic)
-        return dx, dw, None, None
+        return dx, dw, None, None, None
 
 
 class _Router(torch.autograd.Function):
@@ -89,10 +95,14 @@ class _Router(torch.autograd.Function):
         return dx, dw, None
 
 
-def projection(x, w, deterministic=True, out_dtype=torch.bfloat16):
+def projection(x, w, deterministic=True, out_dtype=torch.bfloat16, round_grad_to_bf16=False):
     """y[..., N] = x[..., K] w[N, K]^T with BF16 operands and FP32 accumulation;
-    differentiable in x and w (gradients in BF16)."""
-    return _Projection.apply(x, w, resolve_deterministic(deterministic), out_dtype)
+    differentiable in x and w (gradients in BF16).
+
+    The gradient GEMMs take a BF16 incoming gradient.  With ``out_dtype=float32``
+    the incoming gradient is FP32: backward then raises unless
+    ``round_grad_to_bf16=True``, which rounds it to BF16 (nearest even) first."""
+    return _Projection.apply(x, w, resolve_deterministic(deterministic), out_dtype, bool(round_grad_to_bf16))
 
 
 def router_gating(x, w, deterministic=True):

@@ -97,3 +97,24 @@ def test_checkpointed_step_graph_replays(out_dtype):
     ref = oracle.forward(x2, w)
     rep = budgets.check(host_f64(y), ref, "f32" if out_dtype == torch.float32 else "bf16")
     assert rep["ok"], rep
+
+
+def test_projection_fp32_gradient_rounding_is_explicit():
+    """With an FP32 forward output the incoming gradient is FP32: backward
+    refuses it unless round_grad_to_bf16=True, which equals rounding it to BF16
+    by hand before the gradient entry points."""
+    T, N, K = 128, 256, 512
+    x, w, dy = dpg_inputs.dense(T, N, K, seed_group=9)
+    X = dev_bf16(x).requires_grad_(True)
+    W = dev_bf16(w).requires_grad_(True)
+    g = torch.randn(T, N, device="cuda")
+    y = dag.projection(X, W, out_dtype=torch.float32)
+    assert y.dtype == torch.float32
+    with pytest.raises(TypeError):
+        y.backward(g)
+    y = dag.projection(X, W, out_dtype=torch.float32, round_grad_to_bf16=True)
+    y.backward(g)
+    torch.cuda.synchronize()
+    gb = g.to(torch.bfloat16)
+    assert torch.equal(_bits(X.grad), _bits(dpg.dpg_dgrad(gb, W.detach())))
+    assert torch.equal(_bits(W.grad), _bits(dpg.dpg_wgrad(gb, X.detach())))

@@ -61,3 +61,34 @@ def test_workspace_device_checked():
     host_ws = torch.zeros(1 << 20, dtype=torch.uint8)
     with pytest.raises(ValueError):
         dpg.dpg_wgrad(dy, x, out_dtype=torch.float32, deterministic=False, split_k=2, workspace=host_ws)
+
+
+def test_workspace_lives_on_the_call_stream():
+    """A call on a stream other than the current one: the binding allocates the
+    output and the split workspace on that stream, so memory the current
+    stream allocates and fills right after the call cannot be the workspace
+    the delayed kernels still use.  The result equals a current-stream run bit
+    for bit."""
+    import dpg_inputs
+    from tests.gpu_util import dev_bf16
+    T, N, K = 4031, 64, 4096
+    x, _, dy = dpg_inputs.dense(T, N, K, seed_group=13)
+    X, DY = dev_bf16(x), dev_bf16(dy)
+    ref = dpg.dpg_wgrad(DY, X, out_dtype=torch.float32, deterministic=False, split_k=2)
+    torch.cuda.synchronize()
+    need = dpg.workspace_size(dpg.PASS_WGRAD, T, N, K, torch.float32, False, 2)
+    assert need > 0
+    s = torch.cuda.Stream()
+    big = torch.randn(4096, 4096, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        with torch.cuda.stream(s):
+            for _ in range(8):  # keep stream s busy so the call's kernels start late
+                big = big @ big
+                big = big / big.abs().max()
+        out = dpg.dpg_wgrad(DY, X, out_dtype=torch.float32, deterministic=False, split_k=2, stream=s)
+        junk = torch.empty(need // 4, dtype=torch.float32, device="cuda").fill_(float("nan"))
+        s.synchronize()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32))
+        del junk, out
