@@ -39,3 +39,10 @@ def sample_positions(rows, cols, n, seed=0, edges=True):
             ii.append(np.linspace(0, rows - 1, k).astype(np.int64))
             jj.append(np.full(k, c))
     return np.concatenate(ii).astype(np.int64), np.concatenate(jj).astype(np.int64)
+
+
+def report(tag, **fields):
+    """One line of measured accuracy (error-to-budget margins and the like) on
+    stdout, prefixed PARITY, for runs that collect them (pytest -s)."""
+    import json
+    print("PARITY %s %s" % (tag, json.dumps(fields, sort_keys=True)), flush=True)
