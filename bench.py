@@ -8,15 +8,19 @@ accumulation, BF16 outputs, deterministic plans), inputs resident in HBM.
 ``value`` is the step's TFLOP/s (3 x 2*T*N*K FLOP per step).
 
 Also reported: each pass's microseconds, TFLOP/s and fraction of the BF16 MFMA
-peak; the skinny-N weight gradients (4096->64, 4096->128, 5120->48, 5120->64
-at T = 16384, FP32 out) as GB/s of algorithmic HBM bytes against the 8 TB/s
-peak; the roofline of the dominant kernel from HIP events on the launch
-stream; and the FP64 oracle timed on the host cores on a bounded sample.
+peak, warm (the timed steps) and under the cold-cache protocol (a 1 GiB fill
+before every call, events around the call only, median of 15 groups of 20);
+the skinny-N weight gradients (4096->64, 4096->128, 5120->48, 5120->64 at T =
+1025, 4031, 16173, 16384, 65537, BF16 and FP32 out, planner plan and one and
+two forced splits, cold-cache protocol) as GB/s of algorithmic HBM bytes
+against the 8 TB/s peak; the roofline of the dominant kernel from HIP events
+on the launch stream; and the FP64 oracle timed on the host cores on a
+bounded sample.
 
 Also timed (microseconds, eager and as a captured HIP graph): the 4096->1024
 projection at T = 64, the FP32 router at T = 64 / 256 / 1024 (deterministic
-split-K plans), and the checkpointed FP32 step of 4096->1024 / 4096->512 at
-T = 16384.
+and split-K modes), and the checkpointed FP32 step of 4096->1024 / 4096->512
+at T = 16384, whole and per op.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -36,7 +40,8 @@ PEAK_HBM_GBPS = 8000.0
 T_BIG, N_BIG, K_BIG = 16384, 12288, 4096
 SKINNY = [(4096, 64), (4096, 128), (5120, 48), (5120, 64)]
 # token counts timed: all modes at 16384, the planner's plan also at 65537
-SKINNY_RUNS = [(16384, [(True, 0), (False, 1), (False, 2)]), (65537, [(True, 0)])]
+SKINNY_T_ALL = [1025, 4031, 16173, 16384, 65537]
+SKINNY_MODES = [(True, 0), (False, 1), (False, 2)]   # planner plan, one split, two splits
 SKINNY_T = 16384
 SKINNY_SOURCES = ["deterministic_bf16_projection_amd/csrc/skinny_wgrad.h",
                   "deterministic_bf16_projection_amd/csrc/skinny_direct.h",
@@ -426,29 +431,52 @@ def cpu_oracle_small():
     return out
 
 
-def cold_cache_passes(passes, torch, reps=8):
-    """Each big pass timed alone after a 1 GiB device fill (a cold L2 and
-    Infinity Cache): median microseconds of `reps` runs, HIP events on the
-    launch stream around the pass only."""
-    import numpy as np
-    stream = torch.cuda.current_stream()
-    junk = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+class ColdTimer:
+    """The pages' cold-cache protocol: before every timed call a 1 GiB device
+    buffer is zeroed (more than twice the 32 MB of L2 plus the 256 MB Infinity
+    Cache), HIP events on the launch stream bracket the call only; after
+    warm-ups, `groups` groups of `iters` calls; the result is the median of the
+    per-group medians (microseconds)."""
+
+    def __init__(self, torch, groups=15, iters=20, warmup=5):
+        self.torch = torch
+        self.groups, self.iters, self.warmup = groups, iters, warmup
+        self.junk = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+        n = groups * iters
+        self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    def __call__(self, fn):
+        import numpy as np
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        for _ in range(self.warmup):
+            self.junk.zero_()
+            fn()
+        torch.cuda.synchronize()
+        medians = []
+        for g in range(self.groups):
+            evs = self.ev[g * self.iters:(g + 1) * self.iters]
+            for e0, e1 in evs:
+                self.junk.zero_()
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            medians.append(float(np.median([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])))
+        return float(np.median(medians)), min(medians), max(medians)
+
+    def close(self):
+        del self.junk
+
+
+def cold_cache_passes(passes, cold):
+    """Each big pass under the cold-cache protocol (ColdTimer)."""
     flop = 2.0 * T_BIG * N_BIG * K_BIG
     out = {}
     for name, fn in passes:
-        ts = []
-        for _ in range(reps):
-            junk.zero_()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1) * 1e3)
-        us = float(np.median(ts))
-        out[name] = {"us_median": round(us, 1), "tflops": round(flop / us / 1e6, 1),
-                     "frac_peak": round(flop / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
-    del junk
+        us, lo, hi = cold(fn)
+        out[name] = {"us_median": round(us, 1), "group_median_range_us": [round(lo, 1), round(hi, 1)],
+                     "tflops": round(flop / us / 1e6, 1), "frac_peak": round(flop / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
     return out
 
 
@@ -516,15 +544,67 @@ def config3_more(dpg, torch, X, W, DY, Y, DX, DW, passes):
     return out
 
 
-def secondary_configs(dpg, dpg_inputs, torch, to_dev):
+def skinny_sweep(dpg, dpg_inputs, torch, to_dev, cold):
+    """The skinny-N weight gradients at every (K -> N, T) point, BF16 and FP32
+    output, under the planner's plan and with one and two forced splits, each
+    timed under the cold-cache protocol (ColdTimer).  GB/s are of algorithmic
+    bytes 2TK + 2TN + ob N K (ob = 2 or 4), the split reduction included in the
+    time.  The FP32 planner plans at T = 16384 and 65537 are also timed warm
+    (back to back, operands in the Infinity Cache where they fit) for
+    comparison."""
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    rows = []
+    for T_S in SKINNY_T_ALL:
+        for K, N in SKINNY:
+            xs = to_dev(dpg_inputs.normal_bf16((T_S, K), 1.0, 0, 0))
+            dys = to_dev(dpg_inputs.normal_bf16((T_S, N), 1.0, 0, 2))
+            for out_dtype, ob, oname in ((torch.bfloat16, 2, "bf16"), (torch.float32, 4, "f32")):
+                out = torch.empty((N, K), dtype=out_dtype, device=dev)
+                for det, split in SKINNY_MODES:
+                    ws_n = dpg.workspace_size(dpg.PASS_WGRAD, T_S, N, K, out_dtype, det, split)
+                    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
+                    call = (lambda det=det, split=split, ws=ws, out=out:
+                            dpg.dpg_wgrad(dys, xs, out=out, deterministic=det, split_k=split, workspace=ws))
+                    us, lo, hi = cold(call)
+                    nbytes = 2.0 * T_S * K + 2.0 * T_S * N + ob * N * K
+                    plan = dpg.parse_plan(dpg.plan_describe(dpg.PASS_WGRAD, T_S, N, K, out_dtype, det, split))
+                    row = {"shape": "%d->%d" % (K, N), "T": T_S, "out": oname,
+                           "mode": "planner" if det else "split_k=%d" % split,
+                           "us_cold_median": round(us, 2), "group_median_range_us": [round(lo, 2), round(hi, 2)],
+                           "GBps": round(nbytes / us / 1e3, 1), "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 4),
+                           "splits": int(plan["splits"]), "unit": plan["tile"], "grid": int(plan["grid"])}
+                    if det and oname == "f32" and T_S in (16384, 65537):
+                        reps = 50
+                        for _ in range(5):
+                            call()
+                        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                        e0.record(stream)
+                        for _ in range(reps):
+                            call()
+                        e1.record(stream)
+                        torch.cuda.synchronize()
+                        wus = e0.elapsed_time(e1) * 1e3 / reps
+                        row["us_warm_mean"] = round(wus, 2)
+                        row["GBps_warm"] = round(nbytes / wus / 1e3, 1)
+                    rows.append(row)
+                    del ws
+                del out
+            del xs, dys
+            torch.cuda.empty_cache()
+    return rows
+
+
+def secondary_configs(dpg, dpg_inputs, torch, to_dev, cold):
     """The other measured workloads, microseconds per call: the 4096->1024
     projection at T = 64 (BF16, deterministic), the FP32 router (E = 256,
-    H = 4096) at T = 64 / 256 / 1024 (deterministic split-K plans: the split
-    counts are reported),
-    and the checkpointed step (forward, forward, input gradient, weight
-    gradient; FP32 out) of 4096->1024 and 4096->512 at T = 16384.  Each is
-    timed eagerly (host launch included) and as a captured HIP graph of the
-    same calls (device time only)."""
+    H = 4096) at T = 64 / 256 / 1024 in the deterministic mode and in the
+    split-K mode (the planner's split counts are reported), and the
+    checkpointed step (forward, forward, input gradient, weight gradient; FP32
+    out) of 4096->1024 and 4096->512 at T = 16384, whole and per op (the op
+    alone also under the cold-cache protocol).  Each is timed eagerly (host
+    launch included) and as a captured HIP graph of the same calls (device
+    time only)."""
     import numpy as np
     dev = torch.device("cuda:0")
 
@@ -589,7 +669,8 @@ def secondary_configs(dpg, dpg_inputs, torch, to_dev):
         Yr = torch.empty((T, E), dtype=torch.float32, device=dev)
         DXr = torch.empty((T, H), dtype=torch.float32, device=dev)
         DWr = torch.empty((E, H), dtype=torch.float32, device=dev)
-        for det, split in [(True, 0)]:
+        modes = {}
+        for mode, det, split in [("deterministic", True, 0), ("split_k_mode", False, 0)]:
             w3 = [ws(p, T, E, H, torch.float32, det, split) for p in (3, 4, 5)]
             fwd = lambda: dpg.dpg_router_forward(Xr, Wr, out=Yr, deterministic=det, split_k=split, workspace=w3[0])
             dgr = lambda: dpg.dpg_router_dgrad(DYr, Wr, out=DXr, deterministic=det, split_k=split, workspace=w3[1])
@@ -601,10 +682,12 @@ def secondary_configs(dpg, dpg_inputs, torch, to_dev):
                 rec[name] = {"us_eager": e, "us_graph": g}
             rec["splits"] = {n: int(dpg.parse_plan(dpg.plan_describe(p, T, E, H, torch.float32, det, split))["splits"])
                              for n, p in (("fwd", 3), ("dgrad", 4), ("wgrad", 5))}
-            router["T%d" % T] = rec
+            modes[mode] = rec
+        router["T%d" % T] = modes
     out["router_E256_H4096_f32"] = router
 
-    # checkpointed step, FP32 out
+    # checkpointed step, FP32 out: the step (graph and eager) and each op alone
+    # (warm event mean and the cold-cache median)
     T, K = 16384, 4096
     xs = to_dev(dpg_inputs.normal_bf16((T, K), 1.0, 0, 0))
     step = {}
@@ -615,14 +698,25 @@ def secondary_configs(dpg, dpg_inputs, torch, to_dev):
         DXs = torch.empty((T, K), dtype=torch.float32, device=dev)
         DWs = torch.empty((N, K), dtype=torch.float32, device=dev)
         w3 = [ws(p, T, N, K, torch.float32, True, 0) for p in (0, 1, 2)]
-        calls = [lambda: dpg.dpg_forward(xs, Ws, out=Ys, workspace=w3[0]),
-                 lambda: dpg.dpg_forward(xs, Ws, out=Ys, workspace=w3[0]),
-                 lambda: dpg.dpg_dgrad(DYs, Ws, out=DXs, workspace=w3[1]),
-                 lambda: dpg.dpg_wgrad(DYs, xs, out=DWs, workspace=w3[2])]
+        ops = [("fwd", lambda: dpg.dpg_forward(xs, Ws, out=Ys, workspace=w3[0])),
+               ("dgrad", lambda: dpg.dpg_dgrad(DYs, Ws, out=DXs, workspace=w3[1])),
+               ("wgrad", lambda: dpg.dpg_wgrad(DYs, xs, out=DWs, workspace=w3[2]))]
+        calls = [ops[0][1], ops[0][1], ops[1][1], ops[2][1]]
         e, g = timed(calls, reps=10)
         flop = 8.0 * T * N * K
-        step["4096x%d" % N] = {"us_eager": e, "us_graph": g, "tflops_graph": round(flop / g / 1e6, 1),
-                               "frac_peak_graph": round(flop / g / 1e6 / PEAK_BF16_TFLOPS, 4)}
+        rec = {"us_eager": e, "us_graph": g, "tflops_graph": round(flop / g / 1e6, 1),
+               "frac_peak_graph": round(flop / g / 1e6 / PEAK_BF16_TFLOPS, 4), "ops": {}}
+        flop_op = 2.0 * T * N * K
+        for name, fn in ops:
+            e1, g1 = timed([fn], reps=10)
+            cus, _, _ = cold(fn)
+            p = dpg.parse_plan(dpg.plan_describe({"fwd": 0, "dgrad": 1, "wgrad": 2}[name], T, N, K, torch.float32))
+            rec["ops"][name] = {"us_graph": g1, "tflops_graph": round(flop_op / g1 / 1e6, 1),
+                                "frac_peak_graph": round(flop_op / g1 / 1e6 / PEAK_BF16_TFLOPS, 4),
+                                "us_cold_median": round(cus, 1),
+                                "frac_peak_cold": round(flop_op / cus / 1e6 / PEAK_BF16_TFLOPS, 4),
+                                "plan": "%s %s splits=%s" % (p["kernel"], p["tile"], p["splits"])}
+        step["4096x%d" % N] = rec
         del Ws, DYs, Ys, DXs, DWs
     out["checkpointed_step_T16384_f32"] = step
     return out
@@ -742,41 +836,18 @@ def main():
     busy = read_mfma_busy(dominant)
     if busy:
         roofline["counters"] = busy
-    cold = cold_cache_passes(passes, torch)
+    cold = ColdTimer(torch)
+    passes_cold = cold_cache_passes(passes, cold)
     more = config3_more(dpg, torch, X, W, DY, Y, DX, DW, passes)
 
     skinny = []
     if not args.skip_skinny:
         del Y, DX, DW
         torch.cuda.empty_cache()
-        for T_S, modes in SKINNY_RUNS:
-            for K, N in SKINNY:
-                xs = to_dev(dpg_inputs.normal_bf16((T_S, K), 1.0, 0, 0))
-                dys = to_dev(dpg_inputs.normal_bf16((T_S, N), 1.0, 0, 2))
-                out = torch.empty((N, K), dtype=torch.float32, device=dev)
-                for det, split in modes:
-                    ws_n = dpg.workspace_size(dpg.PASS_WGRAD, T_S, N, K, torch.float32, det, split)
-                    ws = torch.empty(max(ws_n, 16), dtype=torch.uint8, device=dev)
-                    for _ in range(5):
-                        dpg.dpg_wgrad(dys, xs, out=out, deterministic=det, split_k=split, workspace=ws)
-                    reps = 50 if T_S <= 16384 else 20
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    for _ in range(reps):
-                        dpg.dpg_wgrad(dys, xs, out=out, deterministic=det, split_k=split, workspace=ws)
-                    e1.record(stream)
-                    torch.cuda.synchronize()
-                    us = e0.elapsed_time(e1) * 1e3 / reps
-                    nbytes = 2.0 * T_S * K + 2.0 * T_S * N + 4.0 * N * K
-                    skinny.append({"shape": "%d->%d" % (K, N), "T": T_S, "out": "f32",
-                                   "mode": "deterministic, planner splits" if det else "split_k=%d" % split,
-                                   "us": round(us, 2),
-                                   "GBps": round(nbytes / us / 1e3, 1),
-                                   "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 4),
-                                   "plan": dpg.plan_describe(dpg.PASS_WGRAD, T_S, N, K, torch.float32, det, split)})
-                del xs, dys, out
+        skinny = skinny_sweep(dpg, dpg_inputs, torch, to_dev, cold)
 
-    secondary = None if args.skip_secondary else secondary_configs(dpg, dpg_inputs, torch, to_dev)
+    secondary = None if args.skip_secondary else secondary_configs(dpg, dpg_inputs, torch, to_dev, cold)
+    cold.close()
 
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     cpu_small = None if args.no_cpu_baseline else cpu_oracle_small()
@@ -799,7 +870,7 @@ def main():
                    "T": T_BIG, "N": N_BIG, "K": K_BIG, "global_batch": T_BIG, "parallelism": "single GPU"},
         "frac_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "passes": per_pass,
-        "passes_cold_cache": cold,
+        "passes_cold_cache": passes_cold,
         "projection_4096x12288_more": more,
         "skinny_wgrad": skinny,
         "other_workloads": secondary,
