@@ -62,6 +62,10 @@ _lib.dpg_clear_plan_cache.argtypes = []
 _lib.dpg_clear_plan_cache.restype = None
 _lib.dpg_plan_cache_stats.argtypes = [ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
 _lib.dpg_plan_cache_stats.restype = None
+_lib.dpg_wgrad_noalloc.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _ci, _i64, _i64, _i64, _ci, _ci, _vp]
+_lib.dpg_wgrad_noalloc.restype = _ci
+_lib.dpg_noalloc_scratch_bytes.argtypes = []
+_lib.dpg_noalloc_scratch_bytes.restype = _sz
 _lib.dpg_plan_cache_capacity.argtypes = []
 _lib.dpg_plan_cache_capacity.restype = _i64
 _lib.dpg_status_string.argtypes = [_ci]
@@ -280,6 +284,31 @@ def dpg_wgrad(dy, x, out=None, out_dtype=torch.bfloat16, deterministic=True, spl
     _check_out(out, (N, K), dy.device)
     return _call("dpg_wgrad", PASS_WGRAD, dy, x, out, _code(out.dtype), T, N, K, deterministic, split_k,
                  workspace, stream)
+
+
+def dpg_wgrad_noalloc(dy, x, out, deterministic=True, split_k=0, stream=None):
+    """dW[N,K] = dY[T,N]^T X[T,K] into the caller's ``out`` without any
+    allocation: split partials go to the library's static device scratch
+    (``noalloc_scratch_bytes()`` per GPU).  Same plan and bits as dpg_wgrad.
+    Calls that overlap on one GPU race on the scratch; do not issue them."""
+    _check_in(dy, torch.bfloat16, "dy")
+    _check_in(x, torch.bfloat16, "x")
+    T, N = dy.shape
+    K = x.shape[1]
+    if x.shape[0] != T:
+        raise ValueError("x must be [T, K]")
+    _check_same_device(("dy", dy), ("x", x))
+    _check_out(out, (N, K), dy.device)
+    st = _lib.dpg_wgrad_noalloc(dy.data_ptr(), _ld(dy, "dy"), x.data_ptr(), _ld(x, "x"), out.data_ptr(),
+                                _ld(out, "out"), _code(out.dtype), T, N, K, int(bool(deterministic)), split_k,
+                                _stream(stream))
+    if st:
+        raise DpgError(st, "dpg_wgrad_noalloc")
+    return out
+
+
+def noalloc_scratch_bytes():
+    return _lib.dpg_noalloc_scratch_bytes()
 
 
 def dpg_router_forward(x, w, out=None, deterministic=True, split_k=0, workspace=None, stream=None):

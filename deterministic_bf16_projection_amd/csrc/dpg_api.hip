@@ -436,6 +436,41 @@ dpg_status run(int pass, const void* a, int64_t lda, const void* b, int64_t ldb,
 }  // namespace
 }  // namespace dpg
 
+// ------------------------------------------------ no-allocation scratch --
+// Split partials of dpg_wgrad_noalloc live in this array instead of a caller
+// workspace.  Each GPU the library runs on holds its own copy (from the first
+// use of the library's code on that device until the process ends).  Host
+// code never passes the array's name to a kernel: it uses the device address
+// that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[DPG_NOALLOC_SCRATCH_BYTES];
+
+namespace dpg {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {nullptr};
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current); null on failure.
+void* device_scratch() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+}  // namespace dpg
+
 using namespace dpg;
 
 extern "C" {
@@ -460,6 +495,20 @@ dpg_status dpg_wgrad(const void* dy, int64_t lddy, const void* x, int64_t ldx, v
   return run(DPG_PASS_WGRAD, dy, lddy, x, ldx, dw, lddw, dw_dtype, T, N, K, deterministic, split_k, workspace,
              workspace_bytes, stream);
 }
+
+dpg_status dpg_wgrad_noalloc(const void* dy, int64_t lddy, const void* x, int64_t ldx, void* dw, int64_t lddw,
+                             dpg_dtype dw_dtype, int64_t T, int64_t N, int64_t K, int deterministic, int split_k,
+                             hipStream_t stream) {
+  // the plan (and so the bits) of dpg_wgrad; its partials go to the scratch
+  // array, and a plan that needs more than the array holds is refused before
+  // any launch (run() checks the size against the bytes passed here)
+  void* ws = device_scratch();
+  if (!ws) return DPG_ERR_HIP;
+  return run(DPG_PASS_WGRAD, dy, lddy, x, ldx, dw, lddw, dw_dtype, T, N, K, deterministic, split_k, ws,
+             (size_t)DPG_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+size_t dpg_noalloc_scratch_bytes(void) { return (size_t)DPG_NOALLOC_SCRATCH_BYTES; }
 
 dpg_status dpg_router_forward(const float* x, int64_t ldx, const float* w, int64_t ldw, float* y, int64_t ldy,
                               int64_t T, int64_t E, int64_t H, int deterministic, int split_k, void* workspace,

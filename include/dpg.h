@@ -135,6 +135,30 @@ dpg_status dpg_wgrad(const void* dy, int64_t lddy, const void* x, int64_t ldx,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Weight gradient that allocates nothing, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving or training
+ * loops, harnesses that forbid hipMalloc).  Same arguments, plan and output
+ * bits as dpg_wgrad, minus the workspace: the FP32 split partials go to a
+ * static device array of the library, DPG_NOALLOC_SCRATCH_BYTES (64 MiB) per
+ * GPU, held from the library's first use on that GPU until the process ends.
+ * The partial planes are overwritten in full before they are read, so nothing
+ * is cleared between calls.  Every call on one GPU shares that GPU's array:
+ * calls that may overlap on one GPU (different streams, or different host
+ * threads without ordering) race and must not be issued.  A plan whose
+ * partials need more than DPG_NOALLOC_SCRATCH_BYTES (dpg_workspace_size above
+ * it) returns DPG_ERR_WORKSPACE before any launch; DPG_ERR_HIP if the array's
+ * device address cannot be obtained.  Calls no hipMalloc, hipFree or other
+ * allocating routine.
+ */
+#define DPG_NOALLOC_SCRATCH_BYTES (64u << 20)
+dpg_status dpg_wgrad_noalloc(const void* dy, int64_t lddy, const void* x, int64_t ldx,
+                             void* dw, int64_t lddw, dpg_dtype dw_dtype,
+                             int64_t T, int64_t N, int64_t K, int deterministic, int split_k,
+                             hipStream_t stream);
+/* DPG_NOALLOC_SCRATCH_BYTES as the library was built with it. */
+size_t dpg_noalloc_scratch_bytes(void);
+
+/*
  * FP32 router GEMM, E experts (256 on the router page), hidden size H, all
  * operands and outputs FP32 (router page, description and the legend under its
  * ratio table: token-by-hidden activations times a 256-by-hidden weight).  Every product a*b is
