@@ -436,34 +436,61 @@ class ColdTimer:
     buffer is zeroed (more than twice the 32 MB of L2 plus the 256 MB Infinity
     Cache), HIP events on the launch stream bracket the call only; after
     warm-ups, `groups` groups of `iters` calls; the result is the median of the
-    per-group medians (microseconds)."""
+    per-group medians (microseconds).
+
+    flush="read" flushes by reading the 1 GiB buffer instead (a sum): the
+    caches then hold clean lines, whereas after the fill up to ~290 MB of dirty
+    lines (L2 + Infinity Cache) are written back to HBM while the timed call
+    runs, which a short HBM-bound call pays for in full."""
 
     def __init__(self, torch, groups=15, iters=20, warmup=5):
         self.torch = torch
         self.groups, self.iters, self.warmup = groups, iters, warmup
         self.junk = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
+        self.junk.zero_()
         n = groups * iters
         self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
 
-    def __call__(self, fn):
+    def _flush(self, flush):
+        if flush == "zero":
+            self.junk.zero_()
+        else:
+            self.sink = self.junk.sum()
+
+    def __call__(self, fn, flush="zero"):
         import numpy as np
         torch = self.torch
         stream = torch.cuda.current_stream()
         for _ in range(self.warmup):
-            self.junk.zero_()
+            self._flush(flush)
             fn()
         torch.cuda.synchronize()
         medians = []
         for g in range(self.groups):
             evs = self.ev[g * self.iters:(g + 1) * self.iters]
             for e0, e1 in evs:
-                self.junk.zero_()
+                self._flush(flush)
                 e0.record(stream)
                 fn()
                 e1.record(stream)
             torch.cuda.synchronize()
             medians.append(float(np.median([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])))
         return float(np.median(medians)), min(medians), max(medians)
+
+
+def hbm_read_reference(torch, cold):
+    """A plain read of 128 MiB (torch's sum over a BF16 tensor, the X of the
+    4096-wide skinny weight gradients at T = 16384) under both flushes, and a
+    warm back-to-back rate: the HBM read rate a streaming kernel can expect
+    under each protocol."""
+    t = torch.ones((16384, 4096), dtype=torch.bfloat16, device="cuda:0")
+    nbytes = t.numel() * 2
+    out = {}
+    for flush in ("zero", "read"):
+        us, _, _ = cold(lambda: t.sum(), flush=flush)
+        out["cold_%s_flush" % flush] = {"us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1)}
+    del t
+    return out
 
     def close(self):
         del self.junk
@@ -567,12 +594,15 @@ def skinny_sweep(dpg, dpg_inputs, torch, to_dev, cold):
                     call = (lambda det=det, split=split, ws=ws, out=out:
                             dpg.dpg_wgrad(dys, xs, out=out, deterministic=det, split_k=split, workspace=ws))
                     us, lo, hi = cold(call)
+                    rus, _, _ = cold(call, flush="read")
                     nbytes = 2.0 * T_S * K + 2.0 * T_S * N + ob * N * K
                     plan = dpg.parse_plan(dpg.plan_describe(dpg.PASS_WGRAD, T_S, N, K, out_dtype, det, split))
                     row = {"shape": "%d->%d" % (K, N), "T": T_S, "out": oname,
                            "mode": "planner" if det else "split_k=%d" % split,
                            "us_cold_median": round(us, 2), "group_median_range_us": [round(lo, 2), round(hi, 2)],
                            "GBps": round(nbytes / us / 1e3, 1), "frac_hbm": round(nbytes / us / 1e3 / PEAK_HBM_GBPS, 4),
+                           "us_cold_read_flush": round(rus, 2),
+                           "frac_hbm_read_flush": round(nbytes / rus / 1e3 / PEAK_HBM_GBPS, 4),
                            "splits": int(plan["splits"]), "unit": plan["tile"], "grid": int(plan["grid"])}
                     if det and oname == "f32" and T_S in (16384, 65537):
                         reps = 50
@@ -840,11 +870,12 @@ def main():
     passes_cold = cold_cache_passes(passes, cold)
     more = config3_more(dpg, torch, X, W, DY, Y, DX, DW, passes)
 
-    skinny = []
+    skinny, hbm_ref = [], None
     if not args.skip_skinny:
         del Y, DX, DW
         torch.cuda.empty_cache()
         skinny = skinny_sweep(dpg, dpg_inputs, torch, to_dev, cold)
+        hbm_ref = hbm_read_reference(torch, cold)
 
     secondary = None if args.skip_secondary else secondary_configs(dpg, dpg_inputs, torch, to_dev, cold)
     cold.close()
@@ -873,6 +904,7 @@ def main():
         "passes_cold_cache": passes_cold,
         "projection_4096x12288_more": more,
         "skinny_wgrad": skinny,
+        "hbm_read_reference": hbm_ref,
         "other_workloads": secondary,
         "roofline": roofline,
         "cpu_baseline": cpu,
