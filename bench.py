@@ -477,6 +477,9 @@ class ColdTimer:
             medians.append(float(np.median([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])))
         return float(np.median(medians)), min(medians), max(medians)
 
+    def close(self):
+        del self.junk
+
 
 def hbm_read_reference(torch, cold):
     """A plain read of 128 MiB (torch's sum over a BF16 tensor, the X of the
@@ -489,11 +492,18 @@ def hbm_read_reference(torch, cold):
     for flush in ("zero", "read"):
         us, _, _ = cold(lambda: t.sum(), flush=flush)
         out["cold_%s_flush" % flush] = {"us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1)}
+    for _ in range(3):
+        t.sum()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        t.sum()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / 20
+    out["warm"] = {"us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1)}
     del t
     return out
-
-    def close(self):
-        del self.junk
 
 
 def cold_cache_passes(passes, cold):
@@ -628,8 +638,9 @@ def skinny_sweep(dpg, dpg_inputs, torch, to_dev, cold):
 def secondary_configs(dpg, dpg_inputs, torch, to_dev, cold):
     """The other measured workloads, microseconds per call: the 4096->1024
     projection at T = 64 (BF16, deterministic), the FP32 router (E = 256,
-    H = 4096) at T = 64 / 256 / 1024 in the deterministic mode and in the
-    split-K mode (the planner's split counts are reported), and the
+    H = 4096) at T = 64 / 256 / 1024 in the deterministic mode, in the
+    split-K mode and with FP32 fused multiply-adds forced (the plans are
+    reported), and the
     checkpointed step (forward, forward, input gradient, weight gradient; FP32
     out) of 4096->1024 and 4096->512 at T = 16384, whole and per op (the op
     alone also under the cold-cache protocol).  Each is timed eagerly (host
@@ -700,7 +711,8 @@ def secondary_configs(dpg, dpg_inputs, torch, to_dev, cold):
         DXr = torch.empty((T, H), dtype=torch.float32, device=dev)
         DWr = torch.empty((E, H), dtype=torch.float32, device=dev)
         modes = {}
-        for mode, det, split in [("deterministic", True, 0), ("split_k_mode", False, 0)]:
+        for mode, det, split in [("deterministic", True, 0), ("split_k_mode", False, 0), ("fp32fma", True, 0)]:
+            prev_arith = dpg.set_router_arithmetic("fp32" if mode == "fp32fma" else "auto")
             w3 = [ws(p, T, E, H, torch.float32, det, split) for p in (3, 4, 5)]
             fwd = lambda: dpg.dpg_router_forward(Xr, Wr, out=Yr, deterministic=det, split_k=split, workspace=w3[0])
             dgr = lambda: dpg.dpg_router_dgrad(DYr, Wr, out=DXr, deterministic=det, split_k=split, workspace=w3[1])
@@ -710,8 +722,9 @@ def secondary_configs(dpg, dpg_inputs, torch, to_dev, cold):
                                 ("2fwd+bwd", [fwd, fwd, dgr, wgr])]:
                 e, g = timed(calls)
                 rec[name] = {"us_eager": e, "us_graph": g}
-            rec["splits"] = {n: int(dpg.parse_plan(dpg.plan_describe(p, T, E, H, torch.float32, det, split))["splits"])
-                             for n, p in (("fwd", 3), ("dgrad", 4), ("wgrad", 5))}
+            rec["plans"] = {n: "%(kernel)s %(arith)s splits=%(splits)s" % dpg.parse_plan(
+                dpg.plan_describe(p, T, E, H, torch.float32, det, split)) for n, p in (("fwd", 3), ("dgrad", 4), ("wgrad", 5))}
+            dpg.set_router_arithmetic(prev_arith)
             modes[mode] = rec
         router["T%d" % T] = modes
     out["router_E256_H4096_f32"] = router

@@ -66,6 +66,10 @@ _lib.dpg_wgrad_noalloc.argtypes = [_vp, _i64, _vp, _i64, _vp, _i64, _ci, _i64, _
 _lib.dpg_wgrad_noalloc.restype = _ci
 _lib.dpg_noalloc_scratch_bytes.argtypes = []
 _lib.dpg_noalloc_scratch_bytes.restype = _sz
+_lib.dpg_set_router_arithmetic.argtypes = [_ci]
+_lib.dpg_set_router_arithmetic.restype = _ci
+_lib.dpg_get_router_arithmetic.argtypes = []
+_lib.dpg_get_router_arithmetic.restype = _ci
 _lib.dpg_plan_cache_capacity.argtypes = []
 _lib.dpg_plan_cache_capacity.restype = _i64
 _lib.dpg_status_string.argtypes = [_ci]
@@ -170,6 +174,26 @@ def plan_cache_stats():
 
 def plan_cache_capacity():
     return _lib.dpg_plan_cache_capacity()
+
+
+ROUTER_ARITH = {"auto": 0, "bf16x3": 1, "fp32": 2}
+
+
+def set_router_arithmetic(arith):
+    """Process-wide router arithmetic: 'auto' (the planner's choice per shape),
+    'bf16x3' or 'fp32' (FP32 fused multiply-adds).  Returns the previous one."""
+    if arith not in ROUTER_ARITH:
+        raise ValueError("router arithmetic must be one of %s" % sorted(ROUTER_ARITH))
+    prev = get_router_arithmetic()
+    st = _lib.dpg_set_router_arithmetic(ROUTER_ARITH[arith])
+    if st:
+        raise DpgError(st, "dpg_set_router_arithmetic")
+    return prev
+
+
+def get_router_arithmetic():
+    code = _lib.dpg_get_router_arithmetic()
+    return {v: k for k, v in ROUTER_ARITH.items()}[code]
 
 
 def _workspace(pass_, T, N, K, out_code, det, split_k, workspace, device):

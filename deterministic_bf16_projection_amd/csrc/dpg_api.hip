@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 #include <list>
 #include <mutex>
 #include <unordered_map>
@@ -13,6 +14,7 @@
 #include "dpg.h"
 #include "gemm_fast.h"
 #include "gemm_kernel.h"
+#include "gemm_ffma.h"
 #include "skinny_wgrad.h"
 #include "skinny_direct.h"
 #include "skinny_lds.h"
@@ -90,6 +92,17 @@ KernelFn lookup_fast_kernel(int tile, int layout, int x3, int out_kind) {
   return table[tile][layout][out_kind];
 }
 
+// FP32 FMA router kernel for (layout, out kind); FP32 or partial output only
+KernelFn lookup_ffma_kernel(int layout, int out_kind) {
+  static const KernelFn table[3][2] = {
+      {&ffma_kernel<true, true, OUT_F32>, &ffma_kernel<true, true, OUT_PARTIAL>},
+      {&ffma_kernel<true, false, OUT_F32>, &ffma_kernel<true, false, OUT_PARTIAL>},
+      {&ffma_kernel<false, false, OUT_F32>, &ffma_kernel<false, false, OUT_PARTIAL>},
+  };
+  if (layout < 0 || layout > 2 || (out_kind != OUT_F32 && out_kind != OUT_PARTIAL)) return nullptr;
+  return table[layout][out_kind == OUT_F32 ? 0 : 1];
+}
+
 // skinny weight-gradient kernels: (64-row blocks NB, 64-column blocks CB, out kind)
 typedef void (*SkinnyFn)(SkinnyParams);
 template <int NB, int CB>
@@ -148,6 +161,7 @@ struct CacheEntry {
   PlanKey key;
   Plan plan;
 };
+std::atomic<int> g_router_arith{ROUTER_AUTO};
 std::mutex g_mu;
 std::list<CacheEntry>* g_lru = nullptr;  // most recently used first
 std::unordered_map<PlanKey, std::list<CacheEntry>::iterator, KeyHash>* g_index = nullptr;
@@ -201,6 +215,7 @@ PlanKey make_key(int pass, int64_t T, int64_t N, int64_t K, int out, int det, in
   k.det = det ? 1 : 0;
   k.split_req = split_k;
   k.cus = det ? kDetCus : (query_device ? device_cus() : kDetCus);
+  k.router_arith = pass >= 3 ? g_router_arith.load() : ROUTER_AUTO;
   return k;
 }
 
@@ -409,8 +424,9 @@ dpg_status run(int pass, int wlayout, int64_t batch, const void* a, int64_t lda,
     out_kind = out == DPG_BF16 ? OUT_BF16 : OUT_F32;
   }
   const bool fast = plan.fast != 0;
-  KernelFn fn = fast ? lookup_fast_kernel(plan.tile, plan.layout, plan.x3, out_kind)
-                     : (plan.tile == kGenericTile ? lookup_generic_kernel(plan.layout, plan.x3, out_kind) : nullptr);
+  KernelFn fn = plan.ffma ? lookup_ffma_kernel(plan.layout, out_kind)
+                : fast    ? lookup_fast_kernel(plan.tile, plan.layout, plan.x3, out_kind)
+                          : (plan.tile == kGenericTile ? lookup_generic_kernel(plan.layout, plan.x3, out_kind) : nullptr);
   if (!fn) return DPG_ERR_INVALID_ARG;
   void* args[] = {&p};
   const int threads = (fast && plan.tile == 0) ? 512 : 256;
@@ -600,6 +616,14 @@ dpg_status dpg_plan_describe(dpg_pass pass, int64_t T, int64_t N, int64_t K, dpg
   describe_plan(key, plan, buf, buflen);
   return DPG_OK;
 }
+
+dpg_status dpg_set_router_arithmetic(dpg_router_arith arith) {
+  if ((int)arith < DPG_ROUTER_AUTO || (int)arith > DPG_ROUTER_FP32) return DPG_ERR_INVALID_ARG;
+  g_router_arith.store((int)arith);
+  return DPG_OK;
+}
+
+dpg_router_arith dpg_get_router_arithmetic(void) { return (dpg_router_arith)g_router_arith.load(); }
 
 void dpg_clear_plan_cache(void) {
   std::lock_guard<std::mutex> lock(g_mu);

@@ -15,15 +15,18 @@ namespace dpg {
 // against 0.26-0.41 with one depending on layout).  BF16x3 plans use the
 // pipelined 128x128 tile or the generic 64x64 one.
 const TileShape kTiles[kNumTiles] = {
-    // bm, bn, bk, threads, occupancy, eff, eff_one, x3_eff, x3_occupancy, x3_ok, fast_ok
-    {256, 256, 64, 256, 1, 0.55, 0.0, 0.0, 0, false, true},
-    {128, 128, 64, 256, 2, 0.43, 0.36, 0.28, 1, true, true},
-    {64, 64, 64, 256, 4, 0.20, 0.0, 0.19, 2, true, false},
+    // bm, bn, bk, threads, occupancy, eff, eff_one, x3_eff, x3_occupancy, x3_ok, fast_ok, ffma
+    {256, 256, 64, 256, 1, 0.55, 0.0, 0.0, 0, false, true, false},
+    {128, 128, 64, 256, 2, 0.43, 0.36, 0.28, 1, true, true, false},
+    {64, 64, 64, 256, 4, 0.20, 0.0, 0.19, 2, true, false, false},
+    // FP32 FMA (router): eff is the fraction of the CU's FP32 vector rate
+    {64, 64, 64, 256, 4, 0.35, 0.0, 0.0, 0, false, false, true},
 };
 
 namespace {
 
 constexpr double kCuFlops = 2.2e15 / 256;  // sustained BF16 MFMA FLOP/s of one CU (measured loop)
+constexpr double kCuFp32 = 256.0 * 2.4e9;  // FP32 vector FLOP/s of one CU (64 lanes x 4 SIMDs x FMA)
 constexpr double kHbm = 5.0e12;            // sustained HBM bytes/s
 constexpr double kLaunchUs = 3.0;          // per kernel launch
 constexpr double kUnitUs = 1.0;            // fixed latency of a unit (first loads, last MFMAs)
@@ -77,7 +80,7 @@ double estimate_us(const TileShape& ts, bool fast, int64_t batch, int64_t M, int
   const int64_t rounds = cdiv(units, (int64_t)cus * occ_used);
   // a lone four-wave workgroup leaves the CU's MFMA pipes idler than two do
   const double eff = (occ_used == 1 && ts.eff_one > 0) ? ts.eff_one : ts.eff;
-  const double cu_rate = kCuFlops * (x3 ? ts.x3_eff : eff);
+  const double cu_rate = ts.ffma ? kCuFp32 * ts.eff : kCuFlops * (x3 ? ts.x3_eff : eff);
   const double epi_us = (double)occ_used * ts.bm * ts.bn * (s > 1 ? 4 : out_bytes) / kCuStore * 1e6;
   const double mfma_round_us = (double)occ_used * flop_unit / cu_rate * 1e6;
   double t_gemm = fast ? rounds * mfma_round_us + kUnitUs + epi_us : rounds * (mfma_round_us + kUnitUs + epi_us);
@@ -163,15 +166,21 @@ bool make_plan(const PlanKey& key, Plan* p) {
   const bool kmajor_ok = p->layout == LAYOUT_WGRAD || (p->K % 64) == 0;
   double best = 1e300;
   int best_tile = -1;
+  const bool router = key.pass >= 3;
   for (int ti = 0; ti < kNumTiles; ++ti) {
     const TileShape& ts = kTiles[ti];
     const bool fast = ts.fast_ok && kmajor_ok;
-    if (!fast && ti != kGenericTile) continue;
-    if (p->x3 && !ts.x3_ok) continue;
+    if (ts.ffma) {
+      // FP32 FMA: router passes whose arithmetic allows it
+      if (!router || key.router_arith == ROUTER_BF16X3) continue;
+    } else {
+      if (!fast && ti != kGenericTile) continue;
+      if (router && (!ts.x3_ok || key.router_arith == ROUTER_FP32)) continue;
+    }
     for (int c = 0; c < n_choices; ++c) {
       int s, ktp;
-      const double t = estimate_us(ts, fast, p->batch, p->M, p->N, p->K, p->x3, out_bytes, in_bytes, choices[c],
-                                   key.cus, &s, &ktp);
+      const double t = estimate_us(ts, fast, p->batch, p->M, p->N, p->K, ts.ffma ? 0 : p->x3, out_bytes, in_bytes,
+                                   choices[c], key.cus, &s, &ktp);
       if (best_tile < 0 || t < best * 0.97) {  // prefer the earlier (larger tile, fewer splits) unless 3% faster
         best = t;
         best_tile = ti;
@@ -183,11 +192,13 @@ bool make_plan(const PlanKey& key, Plan* p) {
   if (best_tile < 0) return false;
   p->tile = best_tile;
   const TileShape& ts = kTiles[p->tile];
+  if (ts.ffma) p->x3 = 0;
   p->tiles_m = (int)cdiv(p->M, ts.bm);
   p->tiles_n = (int)cdiv(p->N, ts.bn);
   p->kt_total = (int)cdiv(p->K, ts.bk);
   p->group_m = std::min(p->tiles_m, 8);
   p->fast = (ts.fast_ok && kmajor_ok) ? 1 : 0;
+  p->ffma = ts.ffma ? 1 : 0;
   p->grid = (int64_t)p->tiles_m * p->tiles_n * p->splits * p->batch;
   p->ws_bytes = p->splits > 1 ? (size_t)p->batch * p->splits * (size_t)p->M * (size_t)p->N * 4u : 0;
   p->est_us = best;
@@ -195,7 +206,7 @@ bool make_plan(const PlanKey& key, Plan* p) {
 }
 
 bool generic_fallback(Plan* p) {
-  if (p->kind != PLAN_GEMM) return true;
+  if (p->kind != PLAN_GEMM || p->ffma) return true;  // the FP32 FMA kernel addresses with 64 bits
   const TileShape& ts = kTiles[kGenericTile];
   p->tile = kGenericTile;
   p->fast = 0;
@@ -218,14 +229,15 @@ int describe_plan(const PlanKey& key, const Plan& p, char* buf, size_t buflen) {
                     (long long)p.N);
   const TileShape& ts = kTiles[p.tile];
   return snprintf(buf, buflen,
-                  "pass=%s kind=gemm det=%d M=%lld N=%lld K=%lld layout=%s x3=%d out=%s tile=%dx%dx%d threads=%d "
+                  "pass=%s kind=gemm det=%d M=%lld N=%lld K=%lld layout=%s x3=%d arith=%s out=%s tile=%dx%dx%d threads=%d "
                   "kernel=%s tiles=%dx%d group_m=%d splits=%d kt_total=%d kt_per_split=%d grid=%lld workspace=%zu est_us=%.1f "
                   "batch=%lld weight=%s",
                   kPass[key.pass], key.det, (long long)p.M, (long long)p.N, (long long)p.K, kLayout[p.layout], p.x3,
-                  p.out ? "f32" : "bf16", p.skinny ? (int)cdiv(p.M, 64) * 64 : ts.bm, p.skinny ? p.skinny_cols : ts.bn,
+                  p.ffma ? "fp32fma" : (p.x3 ? "bf16x3" : "bf16"), p.out ? "f32" : "bf16", p.skinny ? (int)cdiv(p.M, 64) * 64 : ts.bm, p.skinny ? p.skinny_cols : ts.bn,
                   ts.bk,
                   (p.skinny || (p.fast && p.tile == 0)) ? 512 : ts.threads,
-                  p.skinny ? "skinny" : (p.fast ? "pipelined" : "generic"), p.tiles_m, p.tiles_n, p.group_m, p.splits,
+                  p.skinny ? "skinny" : (p.ffma ? "ffma" : (p.fast ? "pipelined" : "generic")), p.tiles_m, p.tiles_n,
+                  p.group_m, p.splits,
                   p.kt_total, p.kt_per_split, (long long)p.grid, p.ws_bytes, p.est_us, (long long)p.batch,
                   key.wlayout == WEIGHT_KN ? "kn" : "nk");
 }

@@ -21,10 +21,16 @@ struct TileShape {
   int x3_occupancy;  // workgroups per CU with BF16x3 (hi and lo planes)
   bool x3_ok;      // BF16x3 plans use this tile
   bool fast_ok;    // a software-pipelined variant exists for this tile
+  bool ffma;       // FP32 fused multiply-adds on the vector ALUs (router only)
 };
-constexpr int kNumTiles = 3;
-constexpr int kGenericTile = 2;  // the only tile with a generic (non-pipelined) kernel
+constexpr int kNumTiles = 4;
+constexpr int kGenericTile = 2;  // the only tile with a generic (non-pipelined) MFMA kernel
+constexpr int kFfmaTile = 3;     // the FP32 FMA router kernel
 extern const TileShape kTiles[kNumTiles];
+
+// Arithmetic of the router passes: the planner's choice (BF16x3 on the
+// matrix cores, or FP32 FMA where that measured faster), or one of them forced.
+enum RouterArith { ROUTER_AUTO = 0, ROUTER_BF16X3 = 1, ROUTER_FP32 = 2 };
 
 enum WeightLayout { WEIGHT_NK = 0, WEIGHT_KN = 1 };
 
@@ -37,24 +43,26 @@ struct PlanKey {
   int cus;         // CU count the plan was made for (fixed 256 in deterministic mode)
   int64_t batch = 1;         // independent problems of the same shape in one launch
   int wlayout = WEIGHT_NK;   // weight (or weight-gradient) stored [N,K] or [K,N]
+  int router_arith = ROUTER_AUTO;  // router passes only
   int64_t generation = 0;    // plan-cache generation (the planner ignores it)
   bool operator==(const PlanKey& o) const {
     return pass == o.pass && T == o.T && N == o.N && K == o.K && out == o.out && det == o.det &&
            split_req == o.split_req && cus == o.cus && batch == o.batch && wlayout == o.wlayout &&
-           generation == o.generation;
+           router_arith == o.router_arith && generation == o.generation;
   }
 };
 
 struct Plan {
   int kind;
   int layout;          // operand majorness (LAYOUT_*)
-  int x3;              // BF16x3 router arithmetic
+  int x3;              // BF16x3 router arithmetic (0 for the FP32 FMA router kernel)
   int out;             // dpg_dtype of the output
   int64_t M, N, K;     // GEMM view: C[M,N] = sum_k A(m,k) B(n,k)
   int64_t batch;       // problems per launch (the unit stream runs over all of them)
   int swap_ab;         // weight gradient into a [K,N] output: A is X, B is dY
   int tile;            // index into kTiles
   int fast;            // software-pipelined kernel (gemm_fast.h) instead of the generic one
+  int ffma;            // FP32 FMA router kernel (gemm_ffma.h)
   int skinny;          // streaming weight-gradient kernel for N <= 128 (skinny_wgrad.h)
   int skinny_cols;     // columns of K per skinny work unit (64 or 128)
   int tiles_m, tiles_n;

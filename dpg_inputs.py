@@ -50,6 +50,13 @@ def small_int_bf16(shape, seed_group, index):
     return _to_bf16_bits(v)
 
 
+def small_int_f32(shape, seed_group, index):
+    """FP32 values in {-3..3} * 2**-2: products and their partial sums (up to
+    ~10**6 terms) are exact in FP32, so any summation order gives the same bits."""
+    g = _rng(seed_group, index)
+    return g.integers(-3, 4, size=shape).astype(np.float32) * np.float32(0.25)
+
+
 def router_exact_f32(shape, seed_group, index):
     """FP32 values a = hi + lo with hi in {+-1} and lo in {+-1, +-3} * 2**-11.
 
@@ -86,6 +93,10 @@ def router(T, E, H, seed_group=0, kind="normal"):
         x = router_exact_f32((T, H), seed_group, 0)
         w = router_exact_f32((E, H), seed_group, 1)
         dy = router_exact_f32((T, E), seed_group, 2)
+    elif kind == "int":
+        x = small_int_f32((T, H), seed_group, 0)
+        w = small_int_f32((E, H), seed_group, 1)
+        dy = small_int_f32((T, E), seed_group, 2)
     else:
         raise ValueError(kind)
     return x, w, dy

@@ -135,6 +135,28 @@ dpg_status dpg_wgrad(const void* dy, int64_t lddy, const void* x, int64_t ldx,
                      void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Arithmetic of the router passes, a process-wide setting read when a router
+ * call is planned (it is part of the plan key).  The router page's ratio table
+ * shows plain FP32 library calls beating the BF16x3 emulation at small token
+ * counts, and the wgrad page's timeline keeps a router FFMA window; this
+ * library has both:
+ *   DPG_ROUTER_AUTO   : the planner picks, per shape, BF16x3 on the matrix
+ *                       cores or FP32 fused multiply-adds on the vector ALUs
+ *                       (the latter only where it measured faster);
+ *   DPG_ROUTER_BF16X3 : always BF16x3 (hi*hi + hi*lo + lo*hi per product);
+ *   DPG_ROUTER_FP32   : always one FP32 fused multiply-add per product, in
+ *                       ascending order of the reduction index within a split.
+ * Both kinds meet the FP32 budget; they differ from each other in the last
+ * bits.  Each is deterministic in the sense of the conventions above.
+ * DPG_ERR_INVALID_ARG for another value.  Thread-safe; calls already planned
+ * under the previous setting keep their plans only in the cache entries keyed
+ * by that setting.
+ */
+typedef enum { DPG_ROUTER_AUTO = 0, DPG_ROUTER_BF16X3 = 1, DPG_ROUTER_FP32 = 2 } dpg_router_arith;
+dpg_status dpg_set_router_arithmetic(dpg_router_arith arith);
+dpg_router_arith dpg_get_router_arithmetic(void);
+
+/*
  * Weight gradient that allocates nothing, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving or training
  * loops, harnesses that forbid hipMalloc).  Same arguments, plan and output
@@ -164,7 +186,8 @@ size_t dpg_noalloc_scratch_bytes(void);
  * ratio table: token-by-hidden activations times a 256-by-hidden weight).  Every product a*b is
  * computed by BF16x3 emulation: hi = bf16_rne(a), lo = bf16_rne(a - hi), and
  * lo_a*hi_b + hi_a*lo_b + hi_a*hi_b accumulate (in that order) in FP32 on the
- * BF16 matrix cores.
+ * BF16 matrix cores -- or, where dpg_set_router_arithmetic allows it and the
+ * plan takes it, by FP32 fused multiply-adds (see below).
  *   forward: y[T,E]  = x[T,H] . w[E,H]^T
  *   dgrad  : dx[T,H] = dy[T,E] . w[E,H]
  *   wgrad  : dw[E,H] = dy[T,E]^T . x[T,H]

@@ -217,6 +217,34 @@ def test_plan_cache_bounded():
     assert e3 == 0 and g3 == g + 1
 
 
+def test_router_arithmetic_setting():
+    """The router arithmetic setting is part of the plan: 'fp32' plans the FP32
+    FMA kernel (no BF16x3), 'bf16x3' never does, for every router pass, shape
+    and forced split; projection passes ignore the setting; bad values are
+    refused."""
+    prev = dpg.set_router_arithmetic("fp32")
+    try:
+        for T in (64, 256, 1024, 4096):
+            for pass_ in (3, 4, 5):
+                for split in (0, 1, 2, 5):
+                    p = plan(pass_, T, 256, 4096, out=F32, det=1, split=split)
+                    assert p["kernel"] == "ffma" and p["arith"] == "fp32fma" and p["x3"] == "0", p
+                    assert p["tile"] == "64x64x64", p
+                    if split:
+                        assert int(p["splits"]) == min(split, -(-{3: 4096, 4: 256, 5: T}[pass_] // 64)), p
+        assert plan(0, 64, 1024, 4096)["arith"] == "bf16"
+        dpg.set_router_arithmetic("bf16x3")
+        for T in (64, 256, 1024, 4096):
+            for pass_ in (3, 4, 5):
+                p = plan(pass_, T, 256, 4096, out=F32)
+                assert p["kernel"] != "ffma" and p["arith"] == "bf16x3", p
+        assert dpg.get_router_arithmetic() == "bf16x3"
+        assert L.dpg_set_router_arithmetic(7) == 1
+        assert dpg.get_router_arithmetic() == "bf16x3"
+    finally:
+        dpg.set_router_arithmetic(prev)
+
+
 def test_router_uses_bf16x3():
     p = plan(3, 64, 256, 4096, out=F32)
     assert p["x3"] == "1"
