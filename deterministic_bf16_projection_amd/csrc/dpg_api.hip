@@ -92,6 +92,22 @@ KernelFn lookup_fast_kernel(int tile, int layout, int x3, int out_kind) {
   return table[tile][layout][out_kind];
 }
 
+// stream-K variants of the pipelined 256x256 BF16 kernel (BF16 or FP32 output)
+template <int LAYOUT>
+struct StreamKRow {
+  static constexpr KernelFn fns[2] = {
+      &gemm_fast_kernel<256, 256, 2, 4, LAYOUT != LAYOUT_WGRAD, LAYOUT == LAYOUT_FWD, OUT_BF16, false, true>,
+      &gemm_fast_kernel<256, 256, 2, 4, LAYOUT != LAYOUT_WGRAD, LAYOUT == LAYOUT_FWD, OUT_F32, false, true>};
+};
+
+KernelFn lookup_streamk_kernel(int tile, int layout, int out_kind) {
+  static const KernelFn table[3][2] = {{StreamKRow<0>::fns[0], StreamKRow<0>::fns[1]},
+                                       {StreamKRow<1>::fns[0], StreamKRow<1>::fns[1]},
+                                       {StreamKRow<2>::fns[0], StreamKRow<2>::fns[1]}};
+  if (tile != 0 || layout < 0 || layout > 2 || (out_kind != OUT_BF16 && out_kind != OUT_F32)) return nullptr;
+  return table[layout][out_kind];
+}
+
 // FP32 FMA router kernel for (layout, out kind); FP32 or partial output only
 KernelFn lookup_ffma_kernel(int layout, int out_kind) {
   static const KernelFn table[3][2] = {
@@ -392,7 +408,7 @@ dpg_status run(int pass, int wlayout, int64_t batch, const void* a, int64_t lda,
     return DPG_OK;
   }
 
-  GemmParams p;
+  GemmParams p{};
   p.a = a;
   p.b = b;
   p.lda = lda;
@@ -422,6 +438,25 @@ dpg_status run(int pass, int wlayout, int64_t batch, const void* a, int64_t lda,
     p.split_stride = 0;
     p.batch_c = sc;
     out_kind = out == DPG_BF16 ? OUT_BF16 : OUT_F32;
+  }
+  if (plan.streamk) {
+    // stream-K: exactly plan.grid workgroups (the partition depends on it),
+    // then the fix-up of the tail tiles that ranges share
+    p.sk_ws = ws;
+    KernelFn sfn = lookup_streamk_kernel(plan.tile, plan.layout, out_kind);
+    if (!sfn) return DPG_ERR_INVALID_ARG;
+    void* sargs[] = {&p};
+    hipError_t e = hipLaunchKernel((const void*)sfn, dim3((unsigned)plan.grid), dim3(512), sargs, 0, stream);
+    if (e != hipSuccess) return DPG_ERR_HIP;
+    const int tiles = plan.tiles_m * plan.tiles_n;
+    const int G = (int)plan.grid;
+    const int D = (tiles / G) * G;
+    int bm = kTiles[plan.tile].bm, bn = kTiles[plan.tile].bn;
+    void* fargs[] = {&p, &bm, &bn, (void*)&G};
+    e = hipLaunchKernel(out == DPG_BF16 ? (const void*)&streamk_fixup_kernel<OUT_BF16>
+                                        : (const void*)&streamk_fixup_kernel<OUT_F32>,
+                        dim3((unsigned)(std::max(tiles - D, 1) * kStreamKFixupChunks)), dim3(256), fargs, 0, stream);
+    return e == hipSuccess ? DPG_OK : DPG_ERR_HIP;
   }
   const bool fast = plan.fast != 0;
   KernelFn fn = plan.ffma ? lookup_ffma_kernel(plan.layout, out_kind)

@@ -389,11 +389,77 @@ __device__ __forceinline__ StepCursor cursor_next(const UnitMap& m, const StepCu
 
 __device__ __forceinline__ bool cursor_valid(const UnitMap& m, const StepCursor& c) { return c.u < m.total; }
 
+// Stream-K work of one workgroup (deterministic=0 plans; no split of K into
+// planes).  Of the `tiles` output tiles the first D (whole rounds of the grid:
+// D = (tiles / G) G) are data-parallel: workgroup g computes whole tiles g,
+// g + G, ... (XCD-remapped like the unit stream).  The remaining tiles' K
+// iterations (64-wide K tiles) form one sequence that is cut into G even
+// ranges (split_begin over G), range g' = xcd_remap(g) for workgroup g, so
+// every workgroup ends at the same time.
+// A range covers parts of one or two tiles (or whole tiles): a tile covered
+// whole is written out directly, a part goes to partial slot 2 g' (the range's
+// first segment) or 2 g' + 1 (its last), which a fix-up kernel adds in range
+// order, i.e. in ascending K.  A cursor position u counts K iterations along
+// the workgroup's work list: data-parallel tiles first (KT each), then its
+// range.
+struct StreamKWork {
+  int G, D, KT;        // grid, data-parallel tiles, K iterations per tile
+  int dp_count;        // data-parallel tiles of this workgroup
+  int g, i0, i1;       // this workgroup, its range's index and its iterations in the tail sequence
+};
+
+template <int BM, int BN>
+__device__ __forceinline__ void tile_origin(const UnitMap& m, int t, int& row0, int& col0) {
+  const int per_group = m.group_m * m.tiles_n;
+  const int group = t / per_group;
+  const int first_m = group * m.group_m;
+  const int gsize = min(m.tiles_m - first_m, m.group_m);
+  const int r = t - group * per_group;
+  row0 = (first_m + r % gsize) * BM;
+  col0 = (r / gsize) * BN;
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ StepCursor sk_cursor(const UnitMap& m, const StreamKWork& w, int u) {
+  StepCursor c;
+  c.u = u;
+  c.kt = 0;
+  c.b = 0;
+  const int dp_iters = w.dp_count * w.KT;
+  int t;
+  if (u < dp_iters) {
+    t = xcd_remap(w.g + (u / w.KT) * w.G, w.D);
+    c.kt0 = 0;
+    c.nkt = w.KT;
+    c.split = 0;
+  } else {
+    const int i = w.i0 + (u - dp_iters);
+    const int tt = i / w.KT;
+    t = w.D + tt;
+    c.kt0 = i - tt * w.KT;
+    c.nkt = min(w.i1, (tt + 1) * w.KT) - i;
+    c.split = i == w.i0 ? 0 : 1;
+  }
+  tile_origin<BM, BN>(m, min(t, m.tiles_m * m.tiles_n - 1), c.row0, c.col0);
+  return c;
+}
+
+template <int BM, int BN>
+__device__ __forceinline__ StepCursor sk_next(const UnitMap& m, const StreamKWork& w, const StepCursor& c) {
+  if (c.kt + 1 < c.nkt) {
+    StepCursor n = c;
+    n.kt = c.kt + 1;
+    return n;
+  }
+  return sk_cursor<BM, BN>(m, w, c.u + c.nkt);
+}
+
 // Which operands a wave stages: both (four-wave tiles), or only A / only B
 // (eight-wave tiles: waves 0-3 stage A, waves 4-7 stage B).
 enum StageRole { ROLE_BOTH = 0, ROLE_A = 1, ROLE_B = 2 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KMAJ, bool B_KMAJ, int OUT, int ROLE, bool X3 = false>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KMAJ, bool B_KMAJ, int OUT, int ROLE, bool X3 = false,
+          bool SK = false>
 struct FastGemm {
   static constexpr int BK = 64;
   static constexpr int NT = 64 * WAVES_M * WAVES_N;
@@ -431,27 +497,32 @@ struct FastGemm {
   // input gradient of 4096 -> 1024 at 16384 tokens, 189 -> 139 us.
   static __device__ __forceinline__ void epilogue(const GemmParams& p, const StepCursor& c, int lane, int wm, int wn,
                                                   f32x16 (&acc)[FM][FN], char* scr) {
+    char* out;
+    if (OUT == OUT_PARTIAL)
+      out = (char*)p.c + ((int64_t)c.b * p.batch_c + (int64_t)c.split * p.split_stride) * 4;
+    else
+      out = (char*)p.c + (int64_t)c.b * p.batch_c * (OUT == OUT_BF16 ? 2 : 4);
+    store_tile<OUT>(out, p.ldc, 0, 0, p.M, p.N, c.row0, c.col0, lane, wm, wn, acc, scr);
+  }
+
+  // The unit's tile (rows row0.., columns col0..) as EOUT: element (m, n), m <
+  // M and n < N, goes to out + ((m - mo) ldc + (n - no)) elements.
+  template <int EOUT>
+  static __device__ __forceinline__ void store_tile(char* out, int64_t ldc, int mo, int no, int M, int N, int row0,
+                                                    int col0, int lane, int wm, int wn, f32x16 (&acc)[FM][FN],
+                                                    char* scr) {
     static_assert(FN == 2, "a wave's row segment is 64 columns");
     // lane-derived offsets are formed here rather than kept live across the
     // main loop (which would run the MN-major kernels out of registers)
     asm volatile("" : "+v"(lane));
-    char* out;
-    int64_t ldc;
-    if (OUT == OUT_PARTIAL) {
-      out = (char*)p.c + ((int64_t)c.b * p.batch_c + (int64_t)c.split * p.split_stride) * 4;
-      ldc = p.ldc;
-    } else {
-      out = (char*)p.c + (int64_t)c.b * p.batch_c * (OUT == OUT_BF16 ? 2 : 4);
-      ldc = p.ldc;
-    }
     const int lr = lane & 31, lh = lane >> 5;
     const int sw = fswz(lr);
     // read-back: lane l takes row 8 k + l / 8, chunk l % 8; fswz(8 k + rr) = rr ^ k
     const int rr = lane >> 3, cc = lane & 7;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int m0 = c.row0 + wm * WM + i * 32;
-      if constexpr (OUT == OUT_BF16) {
+      const int m0 = row0 + wm * WM + i * 32;
+      if constexpr (EOUT == OUT_BF16) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           // Columns 16 h + [0, 16) of block j: lane l (< 32) holds 16 h + [0, 4)
@@ -476,8 +547,8 @@ struct FastGemm {
         for (int k = 0; k < 4; ++k) {
           const int r = 8 * k + rr;
           const u32x4 v = *(const u32x4*)(scr + r * 128 + ((cc ^ rr ^ k) << 4));
-          const int m = m0 + r, n = c.col0 + wn * WN + cc * 8;
-          if (m < p.M && n < p.N) *(u32x4*)(out + ((int64_t)m * ldc + n) * 2) = v;
+          const int m = m0 + r, n = col0 + wn * WN + cc * 8;
+          if (m < M && n < N) *(u32x4*)(out + ((int64_t)(m - mo) * ldc + (n - no)) * 2) = v;
         }
       } else {
 #pragma unroll
@@ -491,8 +562,8 @@ struct FastGemm {
           for (int k = 0; k < 4; ++k) {
             const int r = 8 * k + rr;
             const f32x4 v = *(const f32x4*)(scr + r * 128 + ((cc ^ rr ^ k) << 4));
-            const int m = m0 + r, n = c.col0 + wn * WN + j * 32 + cc * 4;
-            if (m < p.M && n < p.N) *(f32x4*)(out + ((int64_t)m * ldc + n) * 4) = v;
+            const int m = m0 + r, n = col0 + wn * WN + j * 32 + cc * 4;
+            if (m < M && n < N) *(f32x4*)(out + ((int64_t)(m - mo) * ldc + (n - no)) * 4) = v;
           }
         }
       }
@@ -505,10 +576,36 @@ struct FastGemm {
     const InT* A = (const InT*)p.a;
     const InT* B = (const InT*)p.b;
     const int lda = (int)p.lda, ldb = (int)p.ldb;
+    StreamKWork skw = {};
+    if constexpr (SK) {
+      const int tiles = p.tiles_m * p.tiles_n;
+      skw.G = gridDim.x;
+      skw.KT = p.kt_total;
+      skw.D = (tiles / skw.G) * skw.G;
+      skw.dp_count = skw.D / skw.G;
+      skw.g = blockIdx.x;
+      const SplitParts sp = split_parts(skw.G, (tiles - skw.D) * skw.KT);
+      const int gr = xcd_remap(blockIdx.x, skw.G);
+      skw.i0 = split_begin(gr, sp);
+      skw.i1 = split_begin(gr + 1, sp);
+    }
     const UnitMap um = {p.tiles_m, p.tiles_n, p.group_m, p.splits, p.kt_per_split, p.kt_total,
-                        p.tiles_m * p.tiles_n * p.splits * p.batch, p.tiles_m * p.tiles_n * p.splits,
-                        split_parts(p.splits, p.kt_total)};
+                        SK ? skw.dp_count * skw.KT + (skw.i1 - skw.i0) : p.tiles_m * p.tiles_n * p.splits * p.batch,
+                        p.tiles_m * p.tiles_n * p.splits, split_parts(p.splits, p.kt_total)};
     const int stride = gridDim.x;
+    // the workgroup's unit stream: (tile, K split) units, or its stream-K work
+    auto first_step = [&]() -> StepCursor {
+      if constexpr (SK)
+        return sk_cursor<BM, BN>(um, skw, 0);
+      else
+        return cursor_at<BM, BN>(um, blockIdx.x);
+    };
+    auto next_step = [&](const StepCursor& c) -> StepCursor {
+      if constexpr (SK)
+        return sk_next<BM, BN>(um, skw, c);
+      else
+        return cursor_next<BM, BN>(um, c, stride);
+    };
     OpA opa;
     OpB opb;
     DmaOperand<(ROLE == ROLE_A ? BM : BN), NTL> opd;
@@ -606,22 +703,22 @@ struct FastGemm {
         opd.load(tile_rsrc<true, BN>(B + L.b * p.batch_b, ldb, L.col0, ok ? p.N : L.col0 + 1, kk, p.K), stage + B_BASE);
     };
 
-    StepCursor C = cursor_at<BM, BN>(um, blockIdx.x);
+    StepCursor C = first_step();
     if (!cursor_valid(um, C)) return;
     StepCursor L = C;
     if constexpr (DMA) {
       dma(L, smem);
-      L = cursor_next<BM, BN>(um, L, stride);
+      L = next_step(L);
       __builtin_amdgcn_s_waitcnt(0x0F70);
       __syncthreads();
       dma(L, smem + STAGE);
-      L = cursor_next<BM, BN>(um, L, stride);
+      L = next_step(L);
     } else {
       load(L);
-      L = cursor_next<BM, BN>(um, L, stride);
+      L = next_step(L);
       store(smem);
       load(L);
-      L = cursor_next<BM, BN>(um, L, stride);
+      L = next_step(L);
       __syncthreads();
     }
     DPG_READ_FRAGS(smem, 0, 0);
@@ -679,10 +776,20 @@ struct FastGemm {
       else
         sched_kstep<IGLP, NM / 2, NR, 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
-      L = cursor_next<BM, BN>(um, L, stride);
+      L = next_step(L);
       if (C.kt + 1 >= C.nkt) {
         // the unit is complete: write it while the next unit's loads are in flight
-        epilogue(p, C, lane, wm, wn, acc, scr);
+        if constexpr (SK) {
+          if (C.kt0 == 0 && C.nkt == p.kt_total) {
+            epilogue(p, C, lane, wm, wn, acc, scr);
+          } else {
+            const int gr = xcd_remap(skw.g, skw.G);
+            char* slot = (char*)p.sk_ws + (int64_t)(2 * gr + C.split) * (BM * BN * 4);
+            store_tile<OUT_PARTIAL>(slot, BN, C.row0, C.col0, p.M, p.N, C.row0, C.col0, lane, wm, wn, acc, scr);
+          }
+        } else {
+          epilogue(p, C, lane, wm, wn, acc, scr);
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -690,7 +797,7 @@ struct FastGemm {
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
       }
-      C = cursor_next<BM, BN>(um, C, stride);
+      C = next_step(C);
     }
 #undef DPG_READ_FRAGS
 #undef DPG_READ_A
@@ -699,7 +806,8 @@ struct FastGemm {
   }
 };
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KMAJ, bool B_KMAJ, int OUT, bool X3 = false>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool A_KMAJ, bool B_KMAJ, int OUT, bool X3 = false,
+          bool SK = false>
 __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_fast_kernel(GemmParams p) {
   constexpr int BK = 64;
   constexpr int NT = 64 * WAVES_M * WAVES_N;
@@ -714,11 +822,64 @@ __global__ void __launch_bounds__(64 * WAVES_M * WAVES_N, 1) gemm_fast_kernel(Ge
   const int wm = wave / WAVES_N, wn = wave % WAVES_N;
   if constexpr (NT == 512) {
     if (wave < 4)
-      FastGemm<BM, BN, WAVES_M, WAVES_N, A_KMAJ, B_KMAJ, OUT, ROLE_A>::run(smem, p, tid, lane, wm, wn);
+      FastGemm<BM, BN, WAVES_M, WAVES_N, A_KMAJ, B_KMAJ, OUT, ROLE_A, false, SK>::run(smem, p, tid, lane, wm, wn);
     else
-      FastGemm<BM, BN, WAVES_M, WAVES_N, A_KMAJ, B_KMAJ, OUT, ROLE_B>::run(smem, p, tid - 256, lane, wm, wn);
+      FastGemm<BM, BN, WAVES_M, WAVES_N, A_KMAJ, B_KMAJ, OUT, ROLE_B, false, SK>::run(smem, p, tid - 256, lane, wm, wn);
   } else {
-    FastGemm<BM, BN, WAVES_M, WAVES_N, A_KMAJ, B_KMAJ, OUT, ROLE_BOTH, X3>::run(smem, p, tid, lane, wm, wn);
+    FastGemm<BM, BN, WAVES_M, WAVES_N, A_KMAJ, B_KMAJ, OUT, ROLE_BOTH, X3, SK>::run(smem, p, tid, lane, wm, wn);
+  }
+}
+
+// Stream-K fix-up: each tail tile that two or more ranges share (see
+// StreamKWork) is the sum of their partial slots in range order (ascending
+// K), converted to the output type; other tiles were written by the GEMM
+// kernel.  kStreamKFixupChunks workgroups per tail tile, each a 1/16 of its
+// BM x BN elements (a tail tile can hold the partials of many ranges).
+constexpr int kStreamKFixupChunks = 16;
+
+template <int OUT>
+__global__ void __launch_bounds__(256) streamk_fixup_kernel(GemmParams p, int BM, int BN, int G) {
+  const int tiles = p.tiles_m * p.tiles_n;
+  const int KT = p.kt_total;
+  const int D = (tiles / G) * G;
+  const int t = D + (int)blockIdx.x / kStreamKFixupChunks;
+  const int chunk = (int)blockIdx.x % kStreamKFixupChunks;
+  if (t >= tiles) return;
+  const SplitParts sp = split_parts(G, (tiles - D) * KT);
+  const int a = (t - D) * KT, b = a + KT - 1;
+  // the range holding iteration i: the first r ranges have q + 1 iterations
+  auto owner = [&](int i) {
+    const int big = sp.r * (sp.q + 1);
+    return i < big ? i / (sp.q + 1) : sp.r + (i - big) / sp.q;
+  };
+  const int g0 = owner(a), g1 = owner(b);
+  if (g0 == g1) return;
+  const UnitMap um = {p.tiles_m, p.tiles_n, p.group_m, 1, KT, KT, tiles, tiles, SplitParts{KT, 0}};
+  int row0, col0;
+  tile_origin<1, 1>(um, t, row0, col0);
+  row0 *= BM;
+  col0 *= BN;
+  const float* ws = (const float*)p.sk_ws;
+  const int per_chunk = BM * BN / 4 / kStreamKFixupChunks;
+  for (int e = chunk * per_chunk + threadIdx.x; e < (chunk + 1) * per_chunk; e += 256) {
+    const int r = e / (BN / 4), c4 = (e - r * (BN / 4)) * 4;
+    const int m = row0 + r, n = col0 + c4;
+    if (m >= p.M || n >= p.N) continue;
+    const int64_t off = (int64_t)r * BN + c4;
+    // ranges g0 .. g1 in order; range g's part of this tile is its first
+    // segment (slot 2 g) when the range starts inside the tile, else its last
+    f32x4 v = *(const f32x4*)(ws + (int64_t)(2 * g0 + (split_begin(g0, sp) >= a ? 0 : 1)) * BM * BN + off);
+    for (int g = g0 + 1; g <= g1; ++g) {
+      const f32x4 w = *(const f32x4*)(ws + (int64_t)(2 * g) * BM * BN + off);
+      v[0] += w[0];
+      v[1] += w[1];
+      v[2] += w[2];
+      v[3] += w[3];
+    }
+    if (OUT == OUT_BF16)
+      *(u32x2*)((unsigned short*)p.c + (int64_t)m * p.ldc + n) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+    else
+      *(f32x4*)((float*)p.c + (int64_t)m * p.ldc + n) = v;
   }
 }
 

@@ -38,6 +38,7 @@ struct GemmParams {
   int batch;         // independent problems in the launch (units run over all of them)
   int64_t batch_a, batch_b;  // elements between consecutive problems' A and B
   int64_t batch_c;           // elements between outputs (workspace: splits * split_stride)
+  void* sk_ws;               // stream-K partial slots (stream-K plans only)
 };
 
 template <int BM_, int BN_, int BK_, int WAVES_M_, int WAVES_N_>

@@ -63,6 +63,7 @@ struct Plan {
   int tile;            // index into kTiles
   int fast;            // software-pipelined kernel (gemm_fast.h) instead of the generic one
   int ffma;            // FP32 FMA router kernel (gemm_ffma.h)
+  int streamk;         // stream-K work split over exactly `grid` workgroups (gemm_fast.h StreamKWork)
   int skinny;          // streaming weight-gradient kernel for N <= 128 (skinny_wgrad.h)
   int skinny_cols;     // columns of K per skinny work unit (64 or 128)
   int tiles_m, tiles_n;
@@ -89,8 +90,9 @@ bool make_plan(const PlanKey& key, Plan* plan);
 // Moves a GEMM plan onto the generic 64x64 kernel (64-bit addressing), for
 // calls whose row strides are beyond the pipelined and skinny kernels' 32-bit
 // tile offsets.  The K partition, hence the workspace size and (for one MFMA
-// instruction and k order) the output bits, stays the same.  Returns false if
-// the launch would exceed the grid limit.
+// instruction and k order) the output bits, stays the same; a stream-K plan
+// (split-K mode only) becomes a one-split plan, which needs no more workspace.
+// Returns false if the launch would exceed the grid limit.
 bool generic_fallback(Plan* plan);
 
 // One-line description of a plan.

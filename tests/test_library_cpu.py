@@ -150,7 +150,13 @@ def _check_plan(pass_, T, N, K, out, det, split):
         assert tile in ("256x256x64", "128x128x64"), p
         assert p["x3"] == "0" or tile == "128x128x64", p
     M, Nn = int(p["M"]), int(p["N"])
-    assert int(p["workspace"]) == (s * M * Nn * 4 if s > 1 else 0), p
+    if p["streamk"] == "1":
+        # split-K mode, no forced split: stream-K keeps two FP32 tile slots per workgroup
+        assert split == 0 and det == 0 and s == 1, p
+        bm, bn = (int(v) for v in p["tile"].split("x")[:2])
+        assert int(p["workspace"]) == 2 * int(p["grid"]) * bm * bn * 4, p
+    else:
+        assert int(p["workspace"]) == (s * M * Nn * 4 if s > 1 else 0), p
     assert L.dpg_workspace_size(pass_, T, N, K, out, det, split) == int(p["workspace"])
     return p
 
@@ -215,6 +221,33 @@ def test_plan_cache_bounded():
     dpg.clear_plan_cache()
     e3, g3 = dpg.plan_cache_stats()
     assert e3 == 0 and g3 == g + 1
+
+
+def test_streamk_plans():
+    """Split-K mode takes stream-K on the 256x256 pipelined tile where the last round
+    of tiles would leave most CUs idle (workspace: two FP32 slots of a tile
+    per workgroup; grid: exactly the workgroups the partition is cut for);
+    the deterministic mode, forced split counts, batched calls and the
+    4096->12288 workloads (whole rounds) never take it."""
+    for pass_, T, N, K, tile, G, outs in [(0, 4352, 4096, 4096, 256, 256, (BF16, F32)),
+                                          (0, 8448, 4096, 4096, 256, 256, (BF16, F32)),
+                                          (1, 4352, 4352, 4096, 256, 256, (BF16, F32)),
+                                          (2, 4352, 4352, 4096, 256, 256, (BF16, F32)),
+                                          (0, 4608, 4352, 8192, 256, 256, (BF16, F32))]:
+        for out in outs:
+            p = plan(pass_, T, N, K, out=out, det=0)
+            assert p["streamk"] == "1" and p["kernel"] == "pipelined", p
+            assert p["tile"] == "%dx%dx64" % (tile, tile) and int(p["grid"]) == G, p
+            assert int(p["workspace"]) == 2 * G * tile * tile * 4, p
+            assert L.dpg_workspace_size(pass_, T, N, K, out, 0, 0) == int(p["workspace"])
+            assert plan(pass_, T, N, K, out=out, det=1)["streamk"] == "0"
+            assert plan(pass_, T, N, K, out=out, det=0, split=2)["streamk"] == "0"
+    for pass_ in (0, 1, 2):
+        for T in (16384, 16231):
+            assert plan(pass_, T, 12288, 4096, det=0)["streamk"] == "0"
+    assert _plan_b(0, 2, 4352, 4096, 4096, det=0)["streamk"] == "0"
+    # fewer tiles than workgroups (no whole round) stay with split-K plans
+    assert plan(1, 8448, 4096, 1024, out=F32, det=0)["streamk"] == "0"
 
 
 def test_router_arithmetic_setting():
