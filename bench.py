@@ -81,6 +81,14 @@ def read_traffic(kernel_pass):
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
+def progress(msg):
+    """A progress line on stderr (the JSON result line is the only stdout)."""
+    print("bench: %s (%.0f s)" % (msg, time.time() - _T0), file=sys.stderr, flush=True)
+
+
+_T0 = time.time()
+
+
 def clock_under_load():
     """Engine clock (GHz) measured with rocm-smi under sustained load of the
     forward GEMM (committed summary), or None."""
@@ -112,9 +120,24 @@ PASS_KERNEL_TAG = {  # template arguments (A K-major, B K-major) of each pass's 
 COPY_BYTES = 1 << 30
 
 
+def calibration_kernels(torch, dev):
+    """Kernels of known HBM bytes for scaling FETCH_SIZE / WRITE_SIZE: a 1 GiB
+    device copy (reads and writes 1 GiB) and a sum over another 1 GiB buffer
+    that no kernel has written since it was filled by a 2 GiB sweep (a pure
+    read of 1 GiB)."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    other = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    sweep = torch.empty(2 * COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    sweep.fill_(0.0)  # evicts both buffers from L2 and the Infinity Cache
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    total = other.sum()
+    torch.cuda.synchronize()
+    del src, other, sweep, dst, total
+
+
 def profile_run():
-    """One step of the three passes plus a plain 1 GiB device copy whose HBM
-    bytes are known (used to scale the FETCH_SIZE / WRITE_SIZE counters)."""
+    """One step of the three passes after the calibration kernels."""
     import numpy as np
     import torch
     import dpg_inputs
@@ -124,10 +147,7 @@ def profile_run():
     def to_dev(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
+    calibration_kernels(torch, dev)
     x, w, dy = dpg_inputs.dense(T_BIG, N_BIG, K_BIG, seed_group=0)
     X, W, DY = to_dev(x), to_dev(w), to_dev(dy)
     Y = dpg.dpg_forward(X, W)
@@ -138,8 +158,9 @@ def profile_run():
 
 
 def profile_skinny():
-    """The skinny weight gradients once each (T=16384, FP32 out, planner
-    splits) after a plain 1 GiB device copy (counter calibration)."""
+    """The skinny weight gradients once each (T=16384, FP32 out) under the
+    planner's plan and with one and two forced splits, after the calibration
+    kernels."""
     import numpy as np
     import torch
     import dpg_inputs
@@ -149,24 +170,43 @@ def profile_skinny():
     def to_dev(bits):
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
-    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    del src, dst
+    calibration_kernels(torch, dev)
     for K, N in SKINNY:
         xs = to_dev(dpg_inputs.normal_bf16((SKINNY_T, K), 1.0, 0, 0))
         dys = to_dev(dpg_inputs.normal_bf16((SKINNY_T, N), 1.0, 0, 2))
-        out = dpg.dpg_wgrad(dys, xs, out_dtype=torch.float32)
-        torch.cuda.synchronize()
-        print("skinny %d->%d done" % (K, N), tuple(out.shape), flush=True)
+        for det, split in SKINNY_MODES:
+            out = dpg.dpg_wgrad(dys, xs, out_dtype=torch.float32, deterministic=det, split_k=split)
+            torch.cuda.synchronize()
+            print("skinny %d->%d det=%d split=%d done" % (K, N, det, split), tuple(out.shape), flush=True)
+
+
+def calibration_scales(fetch, write):
+    """Scales that turn FETCH_SIZE / WRITE_SIZE (KB per dispatch) into bytes:
+    the pure 1 GiB read (a sum) for the fetch counter, the 1 GiB copy for the
+    write counter; fetch and write are lists of (kernel name, KB).  Also
+    returns a line describing the calibration (the copy's fetch as a
+    cross-check)."""
+    def biggest(rows, pred):
+        vals = [v for k, v in rows if pred(k.lower()) and "dpg" not in k]
+        if not vals:
+            raise SystemExit("no calibration kernel in the counter file")
+        return max(vals)
+    sum_f = biggest(fetch, lambda k: "reduce_kernel" in k)
+    copy_f = biggest(fetch, lambda k: "copybuffer" in k)
+    copy_w = biggest(write, lambda k: "copybuffer" in k)
+    kb = COPY_BYTES / 1024.0
+    f_scale, w_scale = kb / sum_f, kb / copy_w
+    text = ("calibration: 1 GiB pure read (sum) FETCH_SIZE %.1f KB -> fetch x%.4f; 1 GiB copy WRITE_SIZE %.1f KB -> "
+            "write x%.4f (the copy's FETCH_SIZE %.1f KB, i.e. x%.4f)\n" % (sum_f, f_scale, copy_w, w_scale, copy_f,
+                                                                          kb / copy_f))
+    return f_scale, w_scale, text
 
 
 def summarize_skinny_pmc(fetch_csv, write_csv, command):
     """Writes profiles/skinny_wgrad_T16384_f32_pmc.txt from two rocprofv3 --pmc
     runs of --profile-skinny (FETCH_SIZE, WRITE_SIZE): HBM bytes of each skinny
-    weight gradient (main kernel + split reduction) against its algorithmic
-    bytes."""
+    weight gradient (main kernel + split reduction) under the planner's plan
+    and one and two forced splits, against its algorithmic bytes."""
     import csv
 
     def per_dispatch(path):
@@ -174,37 +214,36 @@ def summarize_skinny_pmc(fetch_csv, write_csv, command):
         for r in csv.DictReader(open(path)):
             e = d.setdefault(int(r["Dispatch_Id"]), [r["Kernel_Name"], 0.0])
             e[1] += float(r["Counter_Value"])
-        return [d[k] for k in sorted(d)]
+        return [tuple(d[k]) for k in sorted(d)]
     fetch, write = per_dispatch(fetch_csv), per_dispatch(write_csv)
-    copy_f = max(v for k, v in fetch if "copybuffer" in k.lower() and "dpg" not in k)
-    copy_w = max(v for k, v in write if "copybuffer" in k.lower() and "dpg" not in k)
-    f_scale, w_scale = (COPY_BYTES / 1024.0) / copy_f, (COPY_BYTES / 1024.0) / copy_w
+    f_scale, w_scale, cal = calibration_scales(fetch, write)
     mine_f = [(k, v) for k, v in fetch if "dpg::" in k]
     mine_w = [(k, v) for k, v in write if "dpg::" in k]
     path = os.path.join(PROFILE_DIR, "skinny_wgrad_T16384_f32_pmc.txt")
     with open(path, "w") as f:
-        f.write("HBM traffic of the skinny weight gradients (T=16384, FP32 out, planner splits), rocprofv3 PMC "
-                "on MI355X\ncommands:\n  %s\n" % command.replace("\n", "\n  "))
+        f.write("HBM traffic of the skinny weight gradients (T=16384, FP32 out; planner plan, split_k=1, split_k=2), "
+                "rocprofv3 PMC on MI355X\ncommands:\n  %s\n" % command.replace("\n", "\n  "))
         f.write("skinny_source_hash: %s\n" % skinny_source_hash())
-        f.write("calibration: 1 GiB device copy read %.1f KB / wrote %.1f KB -> scale fetch x%.4f, write x%.4f\n"
-                % (copy_f, copy_w, f_scale, w_scale))
+        f.write(cal)
         i = 0
         for K, N in SKINNY:
-            tot_f = tot_w = 0.0
-            names = []
-            while i < len(mine_f):
-                k, v = mine_f[i]
-                if names and "reduce" not in k:
-                    break
-                names.append(k.replace("void dpg::", "").split("(")[0])
-                tot_f += v * 1024.0 * f_scale
-                tot_w += mine_w[i][1] * 1024.0 * w_scale
-                i += 1
-                if "reduce" in k:
-                    break
-            alg = 2.0 * SKINNY_T * K + 2.0 * SKINNY_T * N + 4.0 * N * K
-            f.write("%d->%d: fetch %.4g B, write %.4g B, total %.4g B; algorithmic %.4g B (ratio %.3f); kernels: %s\n"
-                    % (K, N, tot_f, tot_w, tot_f + tot_w, alg, (tot_f + tot_w) / alg, " + ".join(names)))
+            for det, split in SKINNY_MODES:
+                tot_f = tot_w = 0.0
+                names = []
+                while i < len(mine_f):
+                    k, v = mine_f[i]
+                    if names and "reduce" not in k:
+                        break
+                    names.append(k.replace("void dpg::", "").split("(")[0])
+                    tot_f += v * 1024.0 * f_scale
+                    tot_w += mine_w[i][1] * 1024.0 * w_scale
+                    i += 1
+                    if "reduce" in k:
+                        break
+                alg = 2.0 * SKINNY_T * K + 2.0 * SKINNY_T * N + 4.0 * N * K
+                f.write("%d->%d %s: fetch %.4g B, write %.4g B, total %.4g B; algorithmic %.4g B (ratio %.3f); "
+                        "kernels: %s\n" % (K, N, "planner" if det else "split_k=%d" % split, tot_f, tot_w,
+                                           tot_f + tot_w, alg, (tot_f + tot_w) / alg, " + ".join(names)))
     print("wrote", path)
 
 
@@ -247,14 +286,7 @@ def summarize_pmc(fetch_csv, write_csv, command):
         vals = [v for (k, c, v, g) in rows if pred(k)]
         return vals
 
-    copy_pred = lambda k: "dpg" not in k and "copybuffer" in k.lower()
-    copy_fetch = pick(fetch, copy_pred)
-    copy_write = pick(write, copy_pred)
-    if not copy_fetch or not copy_write:
-        raise SystemExit("no copy kernel in the counter files")
-    # the largest copy dispatch is the 1 GiB calibration copy
-    f_scale = (COPY_BYTES / 1024.0) / max(copy_fetch)
-    w_scale = (COPY_BYTES / 1024.0) / max(copy_write)
+    f_scale, w_scale, cal = calibration_scales([(k, v) for (k, c, v, g) in fetch], [(k, v) for (k, c, v, g) in write])
     for name, tag in PASS_KERNEL_TAG.items():
         pred = lambda k, tag=tag: "gemm_fast_kernel<256, 256" in k and (", %s," % tag) in k
         fk = pick(fetch, pred)
@@ -271,14 +303,49 @@ def summarize_pmc(fetch_csv, write_csv, command):
             f.write("HBM traffic of the %s GEMM kernel (4096->12288, T=16384, BF16 out), rocprofv3 PMC on MI355X\n" % name)
             f.write("commands:\n  %s\n" % command.replace("\n", "\n  "))
             f.write("kernel_source_hash: %s\n" % kernel_source_hash())
-            f.write("calibration: 1 GiB device copy read %.1f KB / wrote %.1f KB -> scale fetch x%.4f, write x%.4f\n"
-                    % (max(copy_fetch), max(copy_write), f_scale, w_scale))
+            f.write(cal)
             f.write("FETCH_SIZE raw: %.1f KB   WRITE_SIZE raw: %.1f KB\n" % (fk[-1], wk[-1]))
             f.write("fetch_bytes_per_launch: %.4g\nwrite_bytes_per_launch: %.4g\n" % (fetch_b, write_b))
             f.write("hbm_bytes_per_launch: %.4g\n" % (fetch_b + write_b))
             f.write("algorithmic bytes (operands once + output): %.4g (ratio %.2f)\n"
                     % (alg + out_b, (fetch_b + write_b) / (alg + out_b)))
         print("wrote", path)
+
+
+def summarize_counters(out_name, command, *csvs):
+    """Writes profiles/<out_name> from rocprofv3 --pmc runs of --profile-run:
+    every collected counter of each pass's 4096->12288 GEMM kernel (the last
+    dispatch of it), and the average L2 read latency where
+    TCP_TCC_READ_REQ_LATENCY and TCP_TCC_READ_REQ were collected."""
+    import csv
+    per = {}
+    for path in csvs:
+        disp = {}
+        for r in csv.DictReader(open(path)):
+            d = disp.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"], "dur_us": (int(r["End_Timestamp"]) -
+                                                                                       int(r["Start_Timestamp"])) / 1e3})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        for name, tag in PASS_KERNEL_TAG.items():
+            ds = [d for d in disp.values() if "gemm_fast_kernel<256, 256" in d["name"] and (", %s, 0," % tag) in d["name"]]
+            if ds:
+                per.setdefault(name, {}).update({k: v for k, v in ds[-1].items() if k != "name"})
+    path = os.path.join(PROFILE_DIR, out_name)
+    with open(path, "w") as f:
+        f.write("Memory-path counters of the 4096->12288 GEMM passes (T=16384, BF16 out), rocprofv3 PMC on MI355X\n")
+        f.write("commands (one counter group per run):\n  %s\n" % command.replace("\n", "\n  "))
+        f.write("kernel_source_hash: %s\n" % kernel_source_hash())
+        for name, d in per.items():
+            f.write("%s:" % name)
+            for k in sorted(d):
+                f.write(" %s=%.4g" % (k, d[k]))
+            if d.get("TCP_TCC_READ_REQ_sum"):
+                f.write("  avg_L2_read_latency_cycles=%.0f" % (d.get("TCP_TCC_READ_REQ_LATENCY_sum", 0.0) /
+                                                             d["TCP_TCC_READ_REQ_sum"]))
+            if d.get("TCC_EA0_RDREQ_sum"):
+                f.write("  dram_share_of_L2_misses=%.3f" % (d.get("TCC_EA0_RDREQ_DRAM_sum", 0.0) /
+                                                          d["TCC_EA0_RDREQ_sum"]))
+            f.write("\n")
+    print("wrote", path)
 
 
 def summarize_busy(counter_csv, command, xcds=8, cus=256):
@@ -593,6 +660,7 @@ def skinny_sweep(dpg, dpg_inputs, torch, to_dev, cold):
     stream = torch.cuda.current_stream()
     rows = []
     for T_S in SKINNY_T_ALL:
+        progress("skinny weight gradients, T = %d" % T_S)
         for K, N in SKINNY:
             xs = to_dev(dpg_inputs.normal_bf16((T_S, K), 1.0, 0, 0))
             dys = to_dev(dpg_inputs.normal_bf16((T_S, N), 1.0, 0, 2))
@@ -783,6 +851,8 @@ def main():
     ap.add_argument("--profile-skinny", action="store_true",
                     help="the skinny weight gradients once each after a 1 GiB calibration copy (for rocprofv3)")
     ap.add_argument("--summarize-skinny-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"))
+    ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
+                    help="OUT_NAME COMMAND CSV [CSV ...]: all counters of the GEMM passes")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
@@ -795,6 +865,9 @@ def main():
         return
     if args.summarize_skinny_pmc:
         summarize_skinny_pmc(*args.summarize_skinny_pmc)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
@@ -879,9 +952,12 @@ def main():
     busy = read_mfma_busy(dominant)
     if busy:
         roofline["counters"] = busy
+    progress("timed steps done")
     cold = ColdTimer(torch)
     passes_cold = cold_cache_passes(passes, cold)
+    progress("cold-cache passes done")
     more = config3_more(dpg, torch, X, W, DY, Y, DX, DW, passes)
+    progress("4096->12288 extras done")
 
     skinny, hbm_ref = [], None
     if not args.skip_skinny:
@@ -890,11 +966,14 @@ def main():
         skinny = skinny_sweep(dpg, dpg_inputs, torch, to_dev, cold)
         hbm_ref = hbm_read_reference(torch, cold)
 
+    progress("skinny done")
     secondary = None if args.skip_secondary else secondary_configs(dpg, dpg_inputs, torch, to_dev, cold)
     cold.close()
+    progress("other workloads done")
 
     cpu = None if args.no_cpu_baseline else cpu_baseline()
     cpu_small = None if args.no_cpu_baseline else cpu_oracle_small()
+    progress("cpu baseline done")
 
     line = {
         "metric": "TFLOP/s and % BF16 MFMA peak per pass, 4096->12288 T=16384; skinny wgrad GB/s",
