@@ -476,11 +476,15 @@ struct FastGemm {
   typedef typename std::conditional<X3, FastOperandX3<BM, A_KMAJ, NTL>, FastOperand<BM, A_KMAJ, NTL>>::type OpA;
   typedef typename std::conditional<X3, FastOperandX3<BN, B_KMAJ, NTL>, FastOperand<BN, B_KMAJ, NTL>>::type OpB;
   static constexpr bool DO_A = ROLE != ROLE_B, DO_B = ROLE != ROLE_A;
-  // The input gradient's K-major A (dY) is fetched straight into LDS by the
-  // eight-wave kernel's A waves (no staging registers, no LDS write
-  // instructions): measured 2.7% faster for that pass, while for the forward
-  // pass (both operands K-major) register staging is 4% faster.
-  static constexpr bool DMA = !X3 && ROLE == ROLE_A && A_KMAJ && !B_KMAJ;
+  // A K-major A (X in the forward pass, dY in the input gradient) is fetched
+  // straight into LDS by the eight-wave kernel's A waves: no staging
+  // registers and no LDS write instructions for it, which relieves the LDS
+  // issue queue (the forward's waves waited on LDS instructions about three
+  // times as often as the input gradient's).  Measured 2.7% faster for the
+  // input gradient and 1.8% for the forward (six interleaved repeats of the
+  // 4096 -> 12288 step at 16384 tokens); fetching B that way as well was 4-7%
+  // slower for the forward.
+  static constexpr bool DMA = !X3 && ROLE == ROLE_A && A_KMAJ;
   // k-step scheduling by the compiler's interleave strategy (see sched_kstep)
   static constexpr bool IGLP = !X3 && A_KMAJ && B_KMAJ;
 
