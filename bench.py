@@ -367,6 +367,8 @@ def summarize_busy(counter_csv, command, xcds=8, cus=256):
         f.write("kernel_source_hash: %s\n" % kernel_source_hash())
         f.write("clock = GRBM_GUI_ACTIVE / %d XCDs / duration; mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / "
                 "(GRBM_GUI_ACTIVE / %d x %d CUs x 4 SIMDs)\n" % (xcds, xcds, cus))
+        f.write("(under counter collection the second and third kernels' dispatch durations stretch beyond their "
+                "busy cycles, so their clock figures are low; mfma_busy uses the busy cycles only)\n")
         for name, tag in PASS_KERNEL_TAG.items():
             ds = [d for d in disp.values() if "gemm_fast_kernel<256, 256" in d["name"] and (", %s, 0," % tag) in d["name"]]
             if not ds:
