@@ -109,10 +109,13 @@ def read_mfma_busy(kernel_pass):
     text = open(path).read()
     m = re.search(r"kernel_source_hash:\s*(\S+)", text)
     r = re.search(r"^%s: mfma_busy ([0-9.]+) clock_ghz ([0-9.]+)" % kernel_pass, text, re.M)
-    if not m or not r or m.group(1) != kernel_source_hash():
+    # the clock comes from the forward kernel, the first of the counter run:
+    # the later kernels' dispatch durations stretch under counter collection
+    c = re.search(r"^fwd: mfma_busy [0-9.]+ clock_ghz ([0-9.]+)", text, re.M)
+    if not m or not r or not c or m.group(1) != kernel_source_hash():
         return None
-    return {"mfma_busy": float(r.group(1)), "clock_ghz": float(r.group(2)),
-            "source": "rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE (profiles/)"}
+    return {"mfma_busy": float(r.group(1)), "clock_ghz": float(c.group(1)),
+            "source": "rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE (profiles/); clock of the forward kernel"}
 
 
 PASS_KERNEL_TAG = {  # template arguments (A K-major, B K-major) of each pass's GEMM kernel
