@@ -475,16 +475,33 @@ struct FastGemm {
   typedef typename std::conditional<X3, float, __bf16>::type InT;
   typedef typename std::conditional<X3, FastOperandX3<BM, A_KMAJ, NTL>, FastOperand<BM, A_KMAJ, NTL>>::type OpA;
   typedef typename std::conditional<X3, FastOperandX3<BN, B_KMAJ, NTL>, FastOperand<BN, B_KMAJ, NTL>>::type OpB;
-  static constexpr bool DO_A = ROLE != ROLE_B, DO_B = ROLE != ROLE_A;
-  // A K-major A (X in the forward pass, dY in the input gradient) is fetched
-  // straight into LDS by the eight-wave kernel's A waves: no staging
-  // registers and no LDS write instructions for it, which relieves the LDS
-  // issue queue (the forward's waves waited on LDS instructions about three
-  // times as often as the input gradient's).  Measured 2.7% faster for the
-  // input gradient and 1.8% for the forward (six interleaved repeats of the
-  // 4096 -> 12288 step at 16384 tokens); fetching B that way as well was 4-7%
-  // slower for the forward.
-  static constexpr bool DMA = !X3 && ROLE == ROLE_A && A_KMAJ;
+  // Who stages what.  A K-major A (X in the forward pass, dY in the input
+  // gradient) is fetched straight into LDS (buffer_load ... lds: no staging
+  // registers, no LDS write instructions), which relieves the LDS issue
+  // queue: 2.7% faster for the input gradient, 1.8% for the forward (six
+  // interleaved repeats of the 4096 -> 12288 step at 16384 tokens); fetching
+  // the forward's B that way as well was 4-7% slower.
+  // Waves 0-3 (the A waves) win the issue arbitration against waves 4-7 on
+  // each SIMD: timed inside the kernel, with equal work the A waves spent
+  // about a third of every K tile waiting at the barrier for the B waves.
+  // In the forward the A waves therefore fetch A into LDS and also stage B
+  // through registers, and the B waves only read fragments and issue MFMAs
+  // (A waves' barrier wait 32% -> 9-12%, forward 4-8.5% faster on two
+  // boxes).  In the input gradient the A waves fetch A and the B waves stage
+  // the transposed B: the transpose leaves no registers for the A fetch in
+  // the same wave, and handing B to the A waves while the B waves fetch A
+  // was 5% slower.  With both operands MN-major (the weight gradient) each
+  // role stages its own operand.
+  static constexpr bool A_INTO_LDS = !X3 && ROLE != ROLE_BOTH && A_KMAJ;
+  static constexpr bool DMA = A_INTO_LDS && ROLE == ROLE_A;                      // this wave fetches A
+  static constexpr bool DO_A = !A_INTO_LDS && ROLE != ROLE_B;                    // A through registers
+  static constexpr bool DO_B = (A_INTO_LDS && B_KMAJ) ? ROLE == ROLE_A : ROLE != ROLE_A;  // B through registers
+  // Wait (s_waitcnt encoding) for this wave's own LDS fetch of the next
+  // stage before the barrier; when the wave also stages B, the NLOADS B
+  // loads issued after that fetch (for the K tile after next) stay in
+  // flight: vmcnt retires loads in issue order.
+  static_assert(!(DMA && DO_B) || OpB::NLOADS < 16, "vmcnt field");
+  static constexpr int DMA_DONE = 0x0F70 | (DMA && DO_B ? OpB::NLOADS : 0);
   // k-step scheduling by the compiler's interleave strategy (see sched_kstep)
   static constexpr bool IGLP = !X3 && A_KMAJ && B_KMAJ;
 
@@ -612,13 +629,10 @@ struct FastGemm {
     };
     OpA opa;
     OpB opb;
-    DmaOperand<(ROLE == ROLE_A ? BM : BN), NTL> opd;
-    if constexpr (DMA) {
-      opd.init(ltid, ROLE == ROLE_A ? lda : ldb);
-    } else {
-      if (DO_A) opa.init(ltid, lda);
-      if (DO_B) opb.init(ltid, ldb);
-    }
+    DmaOperand<BM, NTL> opd;
+    if constexpr (DMA) opd.init(ltid, lda);
+    if (DO_A) opa.init(ltid, lda);
+    if (DO_B) opb.init(ltid, ldb);
 
     f32x16 acc[FM][FN];
 #pragma unroll
@@ -701,30 +715,24 @@ struct FastGemm {
     auto dma = [&](const StepCursor& L, __bf16* stage) {
       const bool ok = cursor_valid(um, L);
       const int kk = ok ? (L.kt0 + L.kt) * BK : p.K;
-      if constexpr (ROLE == ROLE_A)
-        opd.load(tile_rsrc<true, BM>(A + L.b * p.batch_a, lda, L.row0, ok ? p.M : L.row0 + 1, kk, p.K), stage);
-      else
-        opd.load(tile_rsrc<true, BN>(B + L.b * p.batch_b, ldb, L.col0, ok ? p.N : L.col0 + 1, kk, p.K), stage + B_BASE);
+      opd.load(tile_rsrc<true, BM>(A + L.b * p.batch_a, lda, L.row0, ok ? p.M : L.row0 + 1, kk, p.K), stage);
     };
 
     StepCursor C = first_step();
     if (!cursor_valid(um, C)) return;
     StepCursor L = C;
-    if constexpr (DMA) {
-      dma(L, smem);
-      L = next_step(L);
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();
-      dma(L, smem + STAGE);
-      L = next_step(L);
-    } else {
-      load(L);
-      L = next_step(L);
+    // prologue: K tile 0 into stage 0, the loads of K tile 1 in flight
+    if constexpr (DMA) dma(L, smem);
+    if constexpr (DO_A || DO_B) load(L);
+    L = next_step(L);
+    if constexpr (DO_A || DO_B) {
       store(smem);
       load(L);
-      L = next_step(L);
-      __syncthreads();
     }
+    if constexpr (DMA) __builtin_amdgcn_s_waitcnt(DMA_DONE);
+    __syncthreads();
+    if constexpr (DMA) dma(L, smem + STAGE);
+    L = next_step(L);
     DPG_READ_FRAGS(smem, 0, 0);
 
     constexpr int NM = FM * FN * (X3 ? 3 : 1);  // MFMAs per k-step
@@ -739,14 +747,14 @@ struct FastGemm {
       DPG_MFMAS(0, 0, FM);
       sched_kstep<IGLP, NM, NR, 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
-      // k-step 1: fragments of step 2.  Waves that stage A (or both operands)
-      // write the next K tile into the other buffer and fetch the one after
-      // next here; waves that stage B do it in k-step 2, so the two waves
-      // sharing a SIMD wait for memory at different times and one of them can
-      // always issue MFMAs.
+      // k-step 1: fragments of step 2.  The A waves (and the four-wave
+      // tile's waves) write their staged registers of the next K tile into
+      // the other buffer and fetch the one after next here; B waves that
+      // stage through registers (weight gradient) do it in k-step 2, so the
+      // two waves sharing a SIMD wait for memory at different times.
       DPG_READ_FRAGS(cur, 2, 0);
       DPG_MFMAS(1, 0, FM);
-      if constexpr (ROLE != ROLE_B && !DMA) {
+      if constexpr (ROLE != ROLE_B && (DO_A || DO_B)) {
         store(nxt);
         load(L);
         sched_kstep<IGLP, NM, NR, NW, NV>();
@@ -757,7 +765,7 @@ struct FastGemm {
       // k-step 2: fragments of step 3
       DPG_READ_FRAGS(cur, 3, 1);
       DPG_MFMAS(0, 0, FM);
-      if constexpr (ROLE == ROLE_B && !DMA) {
+      if constexpr (ROLE == ROLE_B && (DO_A || DO_B)) {
         store(nxt);
         load(L);
         sched_kstep<IGLP, NM, NR, NW, NV>();
@@ -770,7 +778,7 @@ struct FastGemm {
       // keep these MFMAs ahead of the barrier: MFMAs have no side effects, so
       // the scheduler would otherwise sink them past it
       __builtin_amdgcn_sched_barrier(0);
-      if constexpr (DMA) __builtin_amdgcn_s_waitcnt(0x0F70);
+      if constexpr (DMA) __builtin_amdgcn_s_waitcnt(DMA_DONE);
       __syncthreads();
       if constexpr (DMA) dma(L, (__bf16*)cur);
       DPG_READ_FRAGS(nxt, 0, 0);  // garbage after the last step (in-bounds LDS)
