@@ -484,18 +484,21 @@ struct FastGemm {
   // Waves 0-3 (the A waves) win the issue arbitration against waves 4-7 on
   // each SIMD: timed inside the kernel, with equal work the A waves spent
   // about a third of every K tile waiting at the barrier for the B waves.
-  // In the forward the A waves therefore fetch A into LDS and also stage B
-  // through registers, and the B waves only read fragments and issue MFMAs
-  // (A waves' barrier wait 32% -> 9-12%, forward 4-8.5% faster on two
-  // boxes).  In the input gradient the A waves fetch A and the B waves stage
-  // the transposed B: the transpose leaves no registers for the A fetch in
-  // the same wave, and handing B to the A waves while the B waves fetch A
-  // was 5% slower.  With both operands MN-major (the weight gradient) each
-  // role stages its own operand.
+  // Where A is K-major the A waves therefore fetch A into LDS and also stage
+  // B through registers, and the B waves only read fragments and issue MFMAs
+  // (forward: A waves' barrier wait 32% -> 9-12%, 4-8.5% faster on two
+  // boxes; input gradient 5.5% faster).  With both operands MN-major (the
+  // weight gradient) each role stages its own operand: the A waves have no
+  // registers for both transposed operands (23 VGPRs spilled, 60% slower).
   static constexpr bool A_INTO_LDS = !X3 && ROLE != ROLE_BOTH && A_KMAJ;
-  static constexpr bool DMA = A_INTO_LDS && ROLE == ROLE_A;                      // this wave fetches A
-  static constexpr bool DO_A = !A_INTO_LDS && ROLE != ROLE_B;                    // A through registers
-  static constexpr bool DO_B = (A_INTO_LDS && B_KMAJ) ? ROLE == ROLE_A : ROLE != ROLE_A;  // B through registers
+  static constexpr bool DMA = A_INTO_LDS && ROLE == ROLE_A;               // this wave fetches A
+  static constexpr bool DO_A = !A_INTO_LDS && ROLE != ROLE_B;             // A through registers
+  static constexpr bool DO_B = A_INTO_LDS ? ROLE == ROLE_A : ROLE != ROLE_A;  // B through registers
+  // Single-buffered A fragments (each row's fragment of the next k-step is
+  // read right after that row's MFMAs issue; B fragments stay double
+  // buffered): 16 fewer VGPRs, which the input gradient's A waves need to
+  // hold the dY fetch and the transposed W staging together.
+  static constexpr bool SB = A_INTO_LDS && !B_KMAJ;
   // Wait (s_waitcnt encoding) for this wave's own LDS fetch of the next
   // stage before the barrier; when the wave also stages B, the NLOADS B
   // loads issued after that fetch (for the K tile after next) stay in
@@ -733,7 +736,21 @@ struct FastGemm {
     __syncthreads();
     if constexpr (DMA) dma(L, smem + STAGE);
     L = next_step(L);
-    DPG_READ_FRAGS(smem, 0, 0);
+    bf16x8 fa1[FM];  // single-buffered A fragments (SB)
+#define DPG_SB_READ_B(stage, S, BUF)                                                                       \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j) fb[BUF][j] =                                              \
+      as_bf16x8(*(const u32x4*)((stage) + b_row[j] + koff[(S) ^ (2 * (j & 1))]))
+#define DPG_SB_READ_A(stage, S, i) \
+  fa1[i] = as_bf16x8(*(const u32x4*)((stage) + a_row[i] + koff[(S) ^ (2 * ((i) & 1))]))
+#define DPG_SB_ROW(BUF, i) \
+  _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(fb[BUF][j], fa1[i], acc[i][j])
+    if constexpr (SB) {
+      DPG_SB_READ_B(smem, 0, 0);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) DPG_SB_READ_A(smem, 0, i);
+    } else {
+      DPG_READ_FRAGS(smem, 0, 0);
+    }
 
     constexpr int NM = FM * FN * (X3 ? 3 : 1);  // MFMAs per k-step
     constexpr int NR = (FM + FN) * PLANES;        // fragment reads per k-step
@@ -742,52 +759,90 @@ struct FastGemm {
     for (int it = 0; cursor_valid(um, C); ++it) {
       const __bf16* cur = smem + (it & 1) * STAGE;
       __bf16* nxt = smem + ((it + 1) & 1) * STAGE;
-      // k-step 0: fragments of step 1 while the MFMAs of step 0 issue
-      DPG_READ_FRAGS(cur, 1, 1);
-      DPG_MFMAS(0, 0, FM);
-      sched_kstep<IGLP, NM, NR, 0, 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      // k-step 1: fragments of step 2.  The A waves (and the four-wave
-      // tile's waves) write their staged registers of the next K tile into
-      // the other buffer and fetch the one after next here; B waves that
-      // stage through registers (weight gradient) do it in k-step 2, so the
-      // two waves sharing a SIMD wait for memory at different times.
-      DPG_READ_FRAGS(cur, 2, 0);
-      DPG_MFMAS(1, 0, FM);
-      if constexpr (ROLE != ROLE_B && (DO_A || DO_B)) {
-        store(nxt);
-        load(L);
-        sched_kstep<IGLP, NM, NR, NW, NV>();
+      if constexpr (SB) {
+        // k-steps 0-2: the next step's B fragments, then row by row the MFMAs
+        // and the next step's A fragment of that row; the A waves stage in
+        // k-step 1
+#pragma unroll
+        for (int s = 0; s < 3; ++s) {
+          DPG_SB_READ_B(cur, s + 1, (s + 1) & 1);
+#pragma unroll
+          for (int i = 0; i < FM; ++i) {
+            DPG_SB_ROW(s & 1, i);
+            DPG_SB_READ_A(cur, s + 1, i);
+          }
+          if (s == 1 && (DO_A || DO_B)) {
+            store(nxt);
+            load(L);
+          }
+          sched_kstep<IGLP, NM, NR, 0, 0>();
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // k-step 3: half the rows, barrier, the next K tile's first fragments
+        // as the other rows' MFMAs issue
+#pragma unroll
+        for (int i = 0; i < FM / 2; ++i) DPG_SB_ROW(1, i);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (DMA) __builtin_amdgcn_s_waitcnt(DMA_DONE);
+        __syncthreads();
+        if constexpr (DMA) dma(L, (__bf16*)cur);
+        DPG_SB_READ_B(nxt, 0, 0);
+#pragma unroll
+        for (int i = 0; i < FM / 2; ++i) DPG_SB_READ_A(nxt, 0, i);
+#pragma unroll
+        for (int i = FM / 2; i < FM; ++i) {
+          DPG_SB_ROW(1, i);
+          DPG_SB_READ_A(nxt, 0, i);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       } else {
+        // k-step 0: fragments of step 1 while the MFMAs of step 0 issue
+        DPG_READ_FRAGS(cur, 1, 1);
+        DPG_MFMAS(0, 0, FM);
         sched_kstep<IGLP, NM, NR, 0, 0>();
+        __builtin_amdgcn_sched_barrier(0);
+        // k-step 1: fragments of step 2.  The A waves (and the four-wave
+        // tile's waves) write their staged registers of the next K tile into
+        // the other buffer and fetch the one after next here; B waves that
+        // stage through registers (weight gradient) do it in k-step 2, so the
+        // two waves sharing a SIMD wait for memory at different times.
+        DPG_READ_FRAGS(cur, 2, 0);
+        DPG_MFMAS(1, 0, FM);
+        if constexpr (ROLE != ROLE_B && (DO_A || DO_B)) {
+          store(nxt);
+          load(L);
+          sched_kstep<IGLP, NM, NR, NW, NV>();
+        } else {
+          sched_kstep<IGLP, NM, NR, 0, 0>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // k-step 2: fragments of step 3
+        DPG_READ_FRAGS(cur, 3, 1);
+        DPG_MFMAS(0, 0, FM);
+        if constexpr (ROLE == ROLE_B && (DO_A || DO_B)) {
+          store(nxt);
+          load(L);
+          sched_kstep<IGLP, NM, NR, NW, NV>();
+        } else {
+          sched_kstep<IGLP, NM, NR, 0, 0>();
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // k-step 3: half the MFMAs, barrier, first fragments of the next K tile, rest
+        DPG_MFMAS(1, 0, FM / 2);
+        // keep these MFMAs ahead of the barrier: MFMAs have no side effects, so
+        // the scheduler would otherwise sink them past it
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (DMA) __builtin_amdgcn_s_waitcnt(DMA_DONE);
+        __syncthreads();
+        if constexpr (DMA) dma(L, (__bf16*)cur);
+        DPG_READ_FRAGS(nxt, 0, 0);  // garbage after the last step (in-bounds LDS)
+        DPG_MFMAS(1, FM / 2, FM);
+        if constexpr (DMA)
+          sched_kstep<IGLP, NM / 2, NR, 0, decltype(opd)::LOADS>();
+        else
+          sched_kstep<IGLP, NM / 2, NR, 0, 0>();
+        __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      // k-step 2: fragments of step 3
-      DPG_READ_FRAGS(cur, 3, 1);
-      DPG_MFMAS(0, 0, FM);
-      if constexpr (ROLE == ROLE_B && (DO_A || DO_B)) {
-        store(nxt);
-        load(L);
-        sched_kstep<IGLP, NM, NR, NW, NV>();
-      } else {
-        sched_kstep<IGLP, NM, NR, 0, 0>();
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      // k-step 3: half the MFMAs, barrier, first fragments of the next K tile, rest
-      DPG_MFMAS(1, 0, FM / 2);
-      // keep these MFMAs ahead of the barrier: MFMAs have no side effects, so
-      // the scheduler would otherwise sink them past it
-      __builtin_amdgcn_sched_barrier(0);
-      if constexpr (DMA) __builtin_amdgcn_s_waitcnt(DMA_DONE);
-      __syncthreads();
-      if constexpr (DMA) dma(L, (__bf16*)cur);
-      DPG_READ_FRAGS(nxt, 0, 0);  // garbage after the last step (in-bounds LDS)
-      DPG_MFMAS(1, FM / 2, FM);
-      if constexpr (DMA)
-        sched_kstep<IGLP, NM / 2, NR, 0, decltype(opd)::LOADS>();
-      else
-        sched_kstep<IGLP, NM / 2, NR, 0, 0>();
-      __builtin_amdgcn_sched_barrier(0);
       L = next_step(L);
       if (C.kt + 1 >= C.nkt) {
         // the unit is complete: write it while the next unit's loads are in flight
@@ -811,6 +866,9 @@ struct FastGemm {
       }
       C = next_step(C);
     }
+#undef DPG_SB_READ_B
+#undef DPG_SB_READ_A
+#undef DPG_SB_ROW
 #undef DPG_READ_FRAGS
 #undef DPG_READ_A
 #undef DPG_READ_B
