@@ -18,6 +18,11 @@
 //   after next are issued right after the staged registers are written to the
 //   other LDS stage, and the single barrier per tile sits in the middle of the
 //   last step's MFMAs.
+// * A K-major A is fetched straight into LDS (buffer_load ... lds).  In the
+//   eight-wave kernel the staging goes to the waves that win the issue
+//   arbitration (waves 0-3) wherever their registers allow it (forward and
+//   input gradient), and the other four waves only read fragments and issue
+//   MFMAs.
 // * The grid is persistent: each workgroup walks a stream of (problem, tile,
 //   K split) units with the K pipeline running across unit boundaries.
 // * A finished unit is written through a 4 KB per-wave LDS buffer that turns
