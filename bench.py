@@ -57,10 +57,15 @@ def skinny_source_hash():
 
 
 def kernel_source_hash(sources=None):
+    """Hash of the kernel sources' code: comments and whitespace are left out,
+    so that a comment edit does not mark the committed counters stale."""
     h = hashlib.sha256()
     for p in sources or KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
