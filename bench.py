@@ -188,6 +188,92 @@ def profile_skinny():
             print("skinny %d->%d det=%d split=%d done" % (K, N, det, split), tuple(out.shape), flush=True)
 
 
+STEP5_N = (1024, 512)
+STEP5_OPS = ("fwd", "fwd", "dgrad", "wgrad")
+
+
+def profile_step5():
+    """The checkpointed FP32-output step's four ops (forward twice, input and
+    weight gradient; 4096->1024 and 4096->512 at T=16384, deterministic
+    plans) once each after the calibration kernels."""
+    import numpy as np
+    import torch
+    import dpg_inputs
+    import deterministic_bf16_projection_amd as dpg
+    dev = torch.device("cuda:0")
+
+    def to_dev(bits):
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    calibration_kernels(torch, dev)
+    f32 = torch.float32
+    for N in STEP5_N:
+        x, w, dy = dpg_inputs.dense(T_BIG, N, K_BIG, seed_group=0)
+        X, W, DY = to_dev(x), to_dev(w), to_dev(dy)
+        for op in STEP5_OPS:
+            if op == "fwd":
+                dpg.dpg_forward(X, W, out_dtype=f32)
+            elif op == "dgrad":
+                dpg.dpg_dgrad(DY, W, out_dtype=f32)
+            else:
+                dpg.dpg_wgrad(DY, X, out_dtype=f32)
+            torch.cuda.synchronize()
+        print("step 4096->%d done" % N, flush=True)
+
+
+def summarize_step5(fetch_csv, write_csv, busy_csv, command):
+    """Writes profiles/checkpointed_step_T16384_f32_pmc.txt from three
+    rocprofv3 --pmc runs of --profile-step5 (FETCH_SIZE; WRITE_SIZE;
+    SQ_VALU_MFMA_BUSY_CYCLES + GRBM_GUI_ACTIVE): per op, its kernels (from the
+    plan: the GEMM, plus the split reduction when the plan splits K), HBM bytes
+    against the algorithmic ones, and the MFMA-busy fraction of its GEMM."""
+    import csv
+    import torch
+    import deterministic_bf16_projection_amd as dpg
+
+    def dispatches(path):
+        d = {}
+        for r in csv.DictReader(open(path)):
+            e = d.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"]})
+            e[r["Counter_Name"]] = e.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        return [d[k] for k in sorted(d)]
+
+    fetch, write, busy = dispatches(fetch_csv), dispatches(write_csv), dispatches(busy_csv)
+    f_scale, w_scale, cal = calibration_scales([(e["name"], e["FETCH_SIZE"]) for e in fetch],
+                                               [(e["name"], e["WRITE_SIZE"]) for e in write])
+    mine = lambda rows: [e for e in rows if "dpg::" in e["name"]]
+    fetch, write, busy = mine(fetch), mine(write), mine(busy)
+    pass_id = {"fwd": dpg.PASS_FORWARD, "dgrad": dpg.PASS_DGRAD, "wgrad": dpg.PASS_WGRAD}
+    path = os.path.join(PROFILE_DIR, "checkpointed_step_T16384_f32_pmc.txt")
+    i = 0
+    with open(path, "w") as f:
+        f.write("HBM traffic and MFMA busy of the checkpointed step's ops (4096->1024 and 4096->512, T=16384, FP32 "
+                "out, deterministic plans), rocprofv3 PMC on MI355X\ncommands:\n  %s\n" % command.replace("\n", "\n  "))
+        f.write("kernel_source_hash: %s\n" % kernel_source_hash())
+        f.write(cal)
+        f.write("mfma_busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 256 CUs x 4 SIMDs) of the GEMM kernel\n")
+        for N in STEP5_N:
+            for op in STEP5_OPS:
+                plan = dpg.plan_describe(pass_id[op], T_BIG, N, K_BIG, torch.float32, True, 0)
+                splits = int(re.search(r"splits=(\d+)", plan).group(1))
+                n_k = 2 if splits > 1 else 1
+                fb = sum(e["FETCH_SIZE"] for e in fetch[i:i + n_k]) * 1024.0 * f_scale
+                wb = sum(e["WRITE_SIZE"] for e in write[i:i + n_k]) * 1024.0 * w_scale
+                g = busy[i]
+                mb = g["SQ_VALU_MFMA_BUSY_CYCLES"] / (g["GRBM_GUI_ACTIVE"] / 8.0 * 256 * 4)
+                names = " + ".join(e["name"].replace("void dpg::", "").split("(")[0][:60] for e in fetch[i:i + n_k])
+                i += n_k
+                if op == "fwd":
+                    alg = 2.0 * T_BIG * K_BIG + 2.0 * N * K_BIG + 4.0 * T_BIG * N
+                elif op == "dgrad":
+                    alg = 2.0 * T_BIG * N + 2.0 * N * K_BIG + 4.0 * T_BIG * K_BIG
+                else:
+                    alg = 2.0 * T_BIG * N + 2.0 * T_BIG * K_BIG + 4.0 * N * K_BIG
+                f.write("4096->%d %-5s: fetch %.4g B, write %.4g B (%.2fx the algorithmic %.4g B); mfma_busy %.3f; "
+                        "splits %d; kernels: %s\n" % (N, op, fb, wb, (fb + wb) / alg, alg, mb, splits, names))
+    print("wrote", path)
+
+
 def calibration_scales(fetch, write):
     """Scales that turn FETCH_SIZE / WRITE_SIZE (KB per dispatch) into bytes:
     the pure 1 GiB read (a sum) for the fetch counter, the 1 GiB copy for the
@@ -861,6 +947,9 @@ def main():
     ap.add_argument("--profile-skinny", action="store_true",
                     help="the skinny weight gradients once each after a 1 GiB calibration copy (for rocprofv3)")
     ap.add_argument("--summarize-skinny-pmc", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"))
+    ap.add_argument("--profile-step5", action="store_true",
+                    help="the checkpointed step's ops once each after the calibration kernels (for rocprofv3)")
+    ap.add_argument("--summarize-step5", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "BUSY_CSV", "COMMAND"))
     ap.add_argument("--summarize-counters", nargs="+", metavar="ARG",
                     help="OUT_NAME COMMAND CSV [CSV ...]: all counters of the GEMM passes")
     args = ap.parse_args()
@@ -879,6 +968,9 @@ def main():
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return
+    if args.summarize_step5:
+        summarize_step5(*args.summarize_step5)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
               file=sys.stderr)
@@ -889,6 +981,9 @@ def main():
         return
     if args.profile_skinny:
         profile_skinny()
+        return
+    if args.profile_step5:
+        profile_step5()
         return
     if args.clock_load:
         clock_load(args.clock_load)
