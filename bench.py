@@ -123,6 +123,24 @@ def read_mfma_busy(kernel_pass):
             "source": "rocprofv3 SQ_VALU_MFMA_BUSY_CYCLES / GRBM_GUI_ACTIVE (profiles/); clock of the forward kernel"}
 
 
+def read_step5_counters(N, op):
+    """HBM bytes and MFMA busy of one checkpointed-step op (the first of its
+    kind, 4096->N) from the committed rocprofv3 summary, if it was taken from
+    the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, "checkpointed_step_T16384_f32_pmc.txt")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m = re.search(r"kernel_source_hash:\s*(\S+)", text)
+    r = re.search(r"^4096->%d %s\s*: fetch ([0-9.e+]+) B, write ([0-9.e+]+) B \(([0-9.]+)x the algorithmic [^)]*\); "
+                  r"mfma_busy ([0-9.]+)" % (N, op), text, re.M)
+    if not m or not r or m.group(1) != kernel_source_hash():
+        return None
+    return {"hbm_bytes": float(r.group(1)) + float(r.group(2)), "x_algorithmic": float(r.group(3)),
+            "mfma_busy": float(r.group(4)), "source": "rocprofv3 FETCH_SIZE / WRITE_SIZE / SQ_VALU_MFMA_BUSY_CYCLES "
+            "(profiles/)"}
+
+
 PASS_KERNEL_TAG = {  # template arguments (A K-major, B K-major) of each pass's GEMM kernel
     "fwd": "true, true", "dgrad": "true, false", "wgrad": "false, false"}
 COPY_BYTES = 1 << 30
@@ -923,6 +941,9 @@ def secondary_configs(dpg, dpg_inputs, torch, to_dev, cold):
                                 "us_cold_median": round(cus, 1),
                                 "frac_peak_cold": round(flop_op / cus / 1e6 / PEAK_BF16_TFLOPS, 4),
                                 "plan": "%s %s splits=%s" % (p["kernel"], p["tile"], p["splits"])}
+            cnt = read_step5_counters(N, name)
+            if cnt:
+                rec["ops"][name]["counters"] = cnt
         step["4096x%d" % N] = rec
         del Ws, DYs, Ys, DXs, DWs
     out["checkpointed_step_T16384_f32"] = step
