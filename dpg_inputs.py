@@ -105,3 +105,26 @@ def router(T, E, H, seed_group=0, kind="normal"):
 def skinny(T, N, K, seed_group=0):
     """dY[T,N], X[T,K] ~ N(0,1) as BF16 bits (skinny-N weight gradient)."""
     return normal_bf16((T, N), 1.0, seed_group, 2), normal_bf16((T, K), 1.0, seed_group, 0)
+
+
+def int_values(shape, lo, hi, seed_group, index):
+    """Integers drawn uniformly from lo..hi (inclusive), as int32."""
+    return _rng(seed_group, index).integers(lo, hi + 1, size=shape).astype(np.int32)
+
+
+def int_factors(rows, cols, rank, seed_group, index, lo=-2, hi=2):
+    """Integer factors U[rows, rank] and V[rank, cols] drawn from lo..hi; a
+    caller that multiplies them gets an integer matrix of rank <= `rank`."""
+    g = _rng(seed_group, index)
+    u = g.integers(lo, hi + 1, size=(rows, rank)).astype(np.int32)
+    v = g.integers(lo, hi + 1, size=(rank, cols)).astype(np.int32)
+    return u, v
+
+
+def ints_to_bf16_bits(a):
+    """Integers of magnitude <= 256 as BF16 bit patterns (exact: BF16 holds
+    every such integer)."""
+    a = np.asarray(a)
+    if a.size and int(np.abs(a).max()) > 256:
+        raise ValueError("integer beyond the exact BF16 range")
+    return _to_bf16_bits(a.astype(np.float32))

@@ -254,6 +254,68 @@ def test_big_projection_sampled(big_inputs, T, seed):
         del out
 
 
+# Whole outputs at full size, 4096 -> 12288 at T = 16384, in the launch
+# configuration of the timed step (deterministic, planner's plan) and in the
+# split-K / stream-K mode.  One operand of each pass is an integer matrix of
+# rank 16 (the product of two integer factors with entries in -2..2), the
+# other a full-rank integer matrix with entries in -3..3.  Every partial sum is
+# an integer below 2**24, so any accumulation order is exact in FP32 and the
+# whole output has a closed form at O(16) operations per element: the same
+# product regrouped around the rank-16 factor (associativity of exact integer
+# arithmetic), e.g. X W^T = (X V^T) U^T for W = U V.  The factor rows are
+# pairwise distinct (checked), so a misplaced row, column or K tile changes
+# some output element; BF16 outputs are compared with the nearest-even
+# rounding of the exact value.
+FULL_T, FULL_N, FULL_K, FULL_RANK = 16384, 12288, 4096, 16
+
+
+def _low_rank_case(pass_name):
+    T, N, K, R = FULL_T, FULL_N, FULL_K, FULL_RANK
+    f = np.float64
+    if pass_name == "fwd":                  # Y = X W^T, W = U V
+        x = dpg_inputs.int_values((T, K), -3, 3, 21, 0)
+        u, v = dpg_inputs.int_factors(N, K, R, 21, 1)
+        a, b, fac = x, u.astype(f) @ v.astype(f), u
+        ref = (x.astype(f) @ v.T.astype(f)) @ u.T.astype(f)
+    elif pass_name == "dgrad":              # dX = dY W, W = U V
+        dy = dpg_inputs.int_values((T, N), -3, 3, 21, 2)
+        u, v = dpg_inputs.int_factors(N, K, R, 21, 1)
+        a, b, fac = dy, u.astype(f) @ v.astype(f), v.T
+        ref = (dy.astype(f) @ u.astype(f)) @ v.astype(f)
+    else:                                   # dW = dY^T X, X = P Q
+        dy = dpg_inputs.int_values((T, N), -3, 3, 21, 2)
+        p, q = dpg_inputs.int_factors(T, K, R, 21, 3)
+        a, b, fac = dy, p.astype(f) @ q.astype(f), q.T
+        ref = (dy.T.astype(f) @ p.astype(f)) @ q.astype(f)
+    # distinct factor rows: output columns (fwd) / K columns (dgrad, wgrad) differ
+    assert np.unique(fac, axis=0).shape[0] == fac.shape[0]
+    assert np.abs(ref).max() < 2.0 ** 24
+    return dpg_inputs.ints_to_bf16_bits(a), dpg_inputs.ints_to_bf16_bits(b), ref
+
+
+@pytest.mark.parametrize("pass_name", ["fwd", "dgrad", "wgrad"])
+def test_big_projection_whole_output_exact(pass_name):
+    a, b, ref = _low_rank_case(pass_name)
+    da, db = dev_bf16(a), dev_bf16(b)
+    del a, b
+    ref32 = ref.astype(np.float32)
+    ref_bits = oracle.f64_to_bf16(ref)
+    del ref
+    for det, split in [(True, 0), (False, 0)]:
+        out = _run(pass_name, da, db, torch.float32, det=det, split=split)
+        got = out.cpu().numpy()
+        bad = int(np.count_nonzero(got != ref32))
+        report("cfg3_whole", pass_=pass_name, out="f32", det=det, mismatches=bad, elements=got.size)
+        assert bad == 0, (pass_name, det, bad)
+        del out, got
+        out = _run(pass_name, da, db, torch.bfloat16, det=det, split=split)
+        got = host_bits(out)
+        bad = int(np.count_nonzero(got != ref_bits))
+        report("cfg3_whole", pass_=pass_name, out="bf16", det=det, mismatches=bad, elements=got.size)
+        assert bad == 0, (pass_name, det, bad)
+        del out, got
+
+
 # ---------------------------------------------------- skinny-N weight gradient --
 SKINNY = [(4096, 64), (4096, 128), (5120, 48), (5120, 64)]
 SKINNY_T = [1025, 4031, 16173, 16384, 65537]
