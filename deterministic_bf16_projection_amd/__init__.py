@@ -212,14 +212,16 @@ def _workspace(pass_, T, N, K, out_code, det, split_k, workspace, device):
 
 def _call(name, pass_, a, b, out, out_code, T, N, K, deterministic, split_k, workspace, stream):
     det = int(bool(deterministic))
-    with _on_stream(stream, out.device):
-        ws, ws_bytes = _workspace(pass_, T, N, K, out_code, det, split_k, workspace, out.device)
-    fn = getattr(_lib, name)
-    args = [a.data_ptr(), _ld(a, "a"), b.data_ptr(), _ld(b, "b"), out.data_ptr(), _ld(out, "out")]
-    if pass_ < 3:
-        args.append(out_code)
-    args += [T, N, K, det, split_k, ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream)]
-    st = fn(*args)
+    # the library launches on HIP's current device: make it the tensors' one
+    with torch.cuda.device(out.device):
+        with _on_stream(stream, out.device):
+            ws, ws_bytes = _workspace(pass_, T, N, K, out_code, det, split_k, workspace, out.device)
+        fn = getattr(_lib, name)
+        args = [a.data_ptr(), _ld(a, "a"), b.data_ptr(), _ld(b, "b"), out.data_ptr(), _ld(out, "out")]
+        if pass_ < 3:
+            args.append(out_code)
+        args += [T, N, K, det, split_k, ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream)]
+        st = fn(*args)
     if st:
         raise DpgError(st, name)
     return out
@@ -323,9 +325,10 @@ def dpg_wgrad_noalloc(dy, x, out, deterministic=True, split_k=0, stream=None):
         raise ValueError("x must be [T, K]")
     _check_same_device(("dy", dy), ("x", x))
     _check_out(out, (N, K), dy.device)
-    st = _lib.dpg_wgrad_noalloc(dy.data_ptr(), _ld(dy, "dy"), x.data_ptr(), _ld(x, "x"), out.data_ptr(),
-                                _ld(out, "out"), _code(out.dtype), T, N, K, int(bool(deterministic)), split_k,
-                                _stream(stream))
+    with torch.cuda.device(out.device):  # the scratch and the launch of the tensors' device
+        st = _lib.dpg_wgrad_noalloc(dy.data_ptr(), _ld(dy, "dy"), x.data_ptr(), _ld(x, "x"), out.data_ptr(),
+                                    _ld(out, "out"), _code(out.dtype), T, N, K, int(bool(deterministic)), split_k,
+                                    _stream(stream))
     if st:
         raise DpgError(st, "dpg_wgrad_noalloc")
     return out
@@ -472,11 +475,13 @@ def dpg_forward_batched(x, w, out=None, out_dtype=torch.bfloat16, weight_layout=
     w3, sw, ldw = _batched(w, "w", batch)
     o3, so, ldo = _batched(out, "out", batch)
     det = int(bool(deterministic))
-    with _on_stream(stream, x.device):
-        ws, wsb = _batched_ws(PASS_FORWARD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace, x.device)
-    st = _lib.dpg_forward_batched(x3.data_ptr(), ldx, sx, w3.data_ptr(), ldw, sw, wl, o3.data_ptr(), ldo, so,
-                                  _code(out.dtype), batch, T, N, K, det, split_k,
-                                  ws.data_ptr() if ws is not None else None, wsb, _stream(stream))
+    with torch.cuda.device(x.device):
+        with _on_stream(stream, x.device):
+            ws, wsb = _batched_ws(PASS_FORWARD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace,
+                                  x.device)
+        st = _lib.dpg_forward_batched(x3.data_ptr(), ldx, sx, w3.data_ptr(), ldw, sw, wl, o3.data_ptr(), ldo, so,
+                                      _code(out.dtype), batch, T, N, K, det, split_k,
+                                      ws.data_ptr() if ws is not None else None, wsb, _stream(stream))
     if st:
         raise DpgError(st, "dpg_forward_batched")
     return out
@@ -502,11 +507,13 @@ def dpg_dgrad_batched(dy, w, out=None, out_dtype=torch.bfloat16, weight_layout="
     w3, sw, ldw = _batched(w, "w", batch)
     o3, so, ldo = _batched(out, "out", batch)
     det = int(bool(deterministic))
-    with _on_stream(stream, dy.device):
-        ws, wsb = _batched_ws(PASS_DGRAD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace, dy.device)
-    st = _lib.dpg_dgrad_batched(d3.data_ptr(), ldd, sd, w3.data_ptr(), ldw, sw, wl, o3.data_ptr(), ldo, so,
-                                _code(out.dtype), batch, T, N, K, det, split_k,
-                                ws.data_ptr() if ws is not None else None, wsb, _stream(stream))
+    with torch.cuda.device(dy.device):
+        with _on_stream(stream, dy.device):
+            ws, wsb = _batched_ws(PASS_DGRAD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace,
+                                  dy.device)
+        st = _lib.dpg_dgrad_batched(d3.data_ptr(), ldd, sd, w3.data_ptr(), ldw, sw, wl, o3.data_ptr(), ldo, so,
+                                    _code(out.dtype), batch, T, N, K, det, split_k,
+                                    ws.data_ptr() if ws is not None else None, wsb, _stream(stream))
     if st:
         raise DpgError(st, "dpg_dgrad_batched")
     return out
@@ -533,11 +540,13 @@ def dpg_wgrad_batched(dy, x, out=None, out_dtype=torch.bfloat16, weight_layout="
     x3, sx, ldx = _batched(x, "x", batch)
     o3, so, ldo = _batched(out, "out", batch)
     det = int(bool(deterministic))
-    with _on_stream(stream, dy.device):
-        ws, wsb = _batched_ws(PASS_WGRAD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace, dy.device)
-    st = _lib.dpg_wgrad_batched(d3.data_ptr(), ldd, sd, x3.data_ptr(), ldx, sx, o3.data_ptr(), ldo, so, wl,
-                                _code(out.dtype), batch, T, N, K, det, split_k,
-                                ws.data_ptr() if ws is not None else None, wsb, _stream(stream))
+    with torch.cuda.device(dy.device):
+        with _on_stream(stream, dy.device):
+            ws, wsb = _batched_ws(PASS_WGRAD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace,
+                                  dy.device)
+        st = _lib.dpg_wgrad_batched(d3.data_ptr(), ldd, sd, x3.data_ptr(), ldx, sx, o3.data_ptr(), ldo, so, wl,
+                                    _code(out.dtype), batch, T, N, K, det, split_k,
+                                    ws.data_ptr() if ws is not None else None, wsb, _stream(stream))
     if st:
         raise DpgError(st, "dpg_wgrad_batched")
     return out

@@ -163,6 +163,7 @@ struct KeyHash {
     mix((uint64_t)k.cus);
     mix((uint64_t)k.batch);
     mix((uint64_t)k.wlayout);
+    mix((uint64_t)k.router_arith);
     mix((uint64_t)k.generation);
     return (size_t)h;
   }
