@@ -142,6 +142,14 @@ def _on_stream(stream, device):
     return torch.cuda.stream(stream)
 
 
+def _on_device(device):
+    """Context that makes the tensors' device HIP's current one, on which the
+    library launches; a no-op (no device switch) when it already is."""
+    if device.index is None or device.index == torch.cuda.current_device():
+        return contextlib.nullcontext()
+    return torch.cuda.device(device)
+
+
 def workspace_size(pass_, T, N, K, out_dtype=torch.bfloat16, deterministic=True, split_k=0):
     n = _lib.dpg_workspace_size(pass_, T, N, K, _code(out_dtype), int(bool(deterministic)), split_k)
     if n == ctypes.c_size_t(-1).value:
@@ -212,8 +220,7 @@ def _workspace(pass_, T, N, K, out_code, det, split_k, workspace, device):
 
 def _call(name, pass_, a, b, out, out_code, T, N, K, deterministic, split_k, workspace, stream):
     det = int(bool(deterministic))
-    # the library launches on HIP's current device: make it the tensors' one
-    with torch.cuda.device(out.device):
+    with _on_device(out.device):
         with _on_stream(stream, out.device):
             ws, ws_bytes = _workspace(pass_, T, N, K, out_code, det, split_k, workspace, out.device)
         fn = getattr(_lib, name)
@@ -325,7 +332,7 @@ def dpg_wgrad_noalloc(dy, x, out, deterministic=True, split_k=0, stream=None):
         raise ValueError("x must be [T, K]")
     _check_same_device(("dy", dy), ("x", x))
     _check_out(out, (N, K), dy.device)
-    with torch.cuda.device(out.device):  # the scratch and the launch of the tensors' device
+    with _on_device(out.device):
         st = _lib.dpg_wgrad_noalloc(dy.data_ptr(), _ld(dy, "dy"), x.data_ptr(), _ld(x, "x"), out.data_ptr(),
                                     _ld(out, "out"), _code(out.dtype), T, N, K, int(bool(deterministic)), split_k,
                                     _stream(stream))
@@ -475,7 +482,7 @@ def dpg_forward_batched(x, w, out=None, out_dtype=torch.bfloat16, weight_layout=
     w3, sw, ldw = _batched(w, "w", batch)
     o3, so, ldo = _batched(out, "out", batch)
     det = int(bool(deterministic))
-    with torch.cuda.device(x.device):
+    with _on_device(x.device):
         with _on_stream(stream, x.device):
             ws, wsb = _batched_ws(PASS_FORWARD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace,
                                   x.device)
@@ -507,7 +514,7 @@ def dpg_dgrad_batched(dy, w, out=None, out_dtype=torch.bfloat16, weight_layout="
     w3, sw, ldw = _batched(w, "w", batch)
     o3, so, ldo = _batched(out, "out", batch)
     det = int(bool(deterministic))
-    with torch.cuda.device(dy.device):
+    with _on_device(dy.device):
         with _on_stream(stream, dy.device):
             ws, wsb = _batched_ws(PASS_DGRAD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace,
                                   dy.device)
@@ -540,7 +547,7 @@ def dpg_wgrad_batched(dy, x, out=None, out_dtype=torch.bfloat16, weight_layout="
     x3, sx, ldx = _batched(x, "x", batch)
     o3, so, ldo = _batched(out, "out", batch)
     det = int(bool(deterministic))
-    with torch.cuda.device(dy.device):
+    with _on_device(dy.device):
         with _on_stream(stream, dy.device):
             ws, wsb = _batched_ws(PASS_WGRAD, wl, batch, T, N, K, _code(out.dtype), det, split_k, workspace,
                                   dy.device)
