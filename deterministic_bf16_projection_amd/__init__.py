@@ -142,10 +142,16 @@ def _on_stream(stream, device):
     return torch.cuda.stream(stream)
 
 
+_n_devices = []
+
+
 def _on_device(device):
     """Context that makes the tensors' device HIP's current one, on which the
-    library launches; a no-op (no device switch) when it already is."""
-    if device.index is None or device.index == torch.cuda.current_device():
+    library launches; a no-op (no device switch, no query) when it already is
+    or when only one device is visible."""
+    if not _n_devices:
+        _n_devices.append(torch.cuda.device_count())
+    if _n_devices[0] <= 1 or device.index is None or device.index == torch.cuda.current_device():
         return contextlib.nullcontext()
     return torch.cuda.device(device)
 
