@@ -18,11 +18,11 @@
 //   after next are issued right after the staged registers are written to the
 //   other LDS stage, and the single barrier per tile sits in the middle of the
 //   last step's MFMAs.
-// * A K-major A is fetched straight into LDS (buffer_load ... lds).  In the
-//   eight-wave kernel the staging goes to the waves that win the issue
-//   arbitration (waves 0-3) wherever their registers allow it (forward and
-//   input gradient), and the other four waves only read fragments and issue
-//   MFMAs.
+// * A K-major A is fetched straight into LDS (buffer_load ... lds), and so is
+//   a K-major B where A is (the forward's W).  In the eight-wave kernel the
+//   staging goes to the waves that win the issue arbitration (waves 0-3)
+//   wherever their registers allow it (forward and input gradient), and the
+//   other four waves only read fragments and issue MFMAs.
 // * The grid is persistent: each workgroup walks a stream of (problem, tile,
 //   K split) units with the K pipeline running across unit boundaries.
 // * A finished unit is written through a 4 KB per-wave LDS buffer that turns
@@ -484,21 +484,25 @@ struct FastGemm {
   // gradient) is fetched straight into LDS (buffer_load ... lds: no staging
   // registers, no LDS write instructions), which relieves the LDS issue
   // queue: 2.7% faster for the input gradient, 1.8% for the forward (six
-  // interleaved repeats of the 4096 -> 12288 step at 16384 tokens); fetching
-  // the forward's B that way as well was 4-7% slower.
+  // interleaved repeats of the 4096 -> 12288 step at 16384 tokens).
   // Waves 0-3 (the A waves) win the issue arbitration against waves 4-7 on
   // each SIMD: timed inside the kernel, with equal work the A waves spent
   // about a third of every K tile waiting at the barrier for the B waves.
-  // Where A is K-major the A waves therefore fetch A into LDS and also stage
-  // B through registers, and the B waves only read fragments and issue MFMAs
-  // (forward: A waves' barrier wait 32% -> 9-12%, 4-8.5% faster on two
-  // boxes; input gradient 5.5% faster).  With both operands MN-major (the
-  // weight gradient) each role stages its own operand: the A waves have no
-  // registers for both transposed operands (23 VGPRs spilled, 60% slower).
+  // Where A is K-major the A waves therefore do all the staging and the B
+  // waves only read fragments and issue MFMAs (forward: A waves' barrier wait
+  // 32% -> 9-12%, 4-8.5% faster on two boxes; input gradient 5.5% faster).
+  // In the forward the A waves fetch W straight into LDS as well (the LDS
+  // fetch moves ~44 GB/s per CU from L2 against ~39 through registers): 4%
+  // faster, no W staging registers (204 VGPRs); with the B waves fetching W
+  // instead it was 11% slower.  The input gradient's W is MN-major and stays
+  // on the register path (transposed there).  With both operands MN-major
+  // (the weight gradient) each role stages its own operand: the A waves have
+  // no registers for both transposed operands (23 VGPRs spilled, 60% slower).
   static constexpr bool A_INTO_LDS = !X3 && ROLE != ROLE_BOTH && A_KMAJ;
   static constexpr bool DMA = A_INTO_LDS && ROLE == ROLE_A;               // this wave fetches A
   static constexpr bool DO_A = !A_INTO_LDS && ROLE != ROLE_B;             // A through registers
-  static constexpr bool DO_B = A_INTO_LDS ? ROLE == ROLE_A : ROLE != ROLE_A;  // B through registers
+  static constexpr bool B_INTO_LDS = A_INTO_LDS && B_KMAJ;                // forward: W fetched by the A waves too
+  static constexpr bool DO_B = B_INTO_LDS ? false : (A_INTO_LDS ? ROLE == ROLE_A : ROLE != ROLE_A);  // B through registers
   // Single-buffered A fragments (each row's fragment of the next k-step is
   // read right after that row's MFMAs issue; B fragments stay double
   // buffered): 16 fewer VGPRs, which the input gradient's A waves need to
@@ -638,7 +642,9 @@ struct FastGemm {
     OpA opa;
     OpB opb;
     DmaOperand<BM, NTL> opd;
+    DmaOperand<BN, NTL> opdb;
     if constexpr (DMA) opd.init(ltid, lda);
+    if constexpr (DMA && B_INTO_LDS) opdb.init(ltid, ldb);
     if (DO_A) opa.init(ltid, lda);
     if (DO_B) opb.init(ltid, ldb);
 
@@ -724,6 +730,9 @@ struct FastGemm {
       const bool ok = cursor_valid(um, L);
       const int kk = ok ? (L.kt0 + L.kt) * BK : p.K;
       opd.load(tile_rsrc<true, BM>(A + L.b * p.batch_a, lda, L.row0, ok ? p.M : L.row0 + 1, kk, p.K), stage);
+      if constexpr (B_INTO_LDS)
+        opdb.load(tile_rsrc<true, BN>(B + L.b * p.batch_b, ldb, L.col0, ok ? p.N : L.col0 + 1, kk, p.K),
+                  stage + B_BASE);
     };
 
     StepCursor C = first_step();
@@ -843,7 +852,7 @@ struct FastGemm {
         DPG_READ_FRAGS(nxt, 0, 0);  // garbage after the last step (in-bounds LDS)
         DPG_MFMAS(1, FM / 2, FM);
         if constexpr (DMA)
-          sched_kstep<IGLP, NM / 2, NR, 0, decltype(opd)::LOADS>();
+          sched_kstep<IGLP, NM / 2, NR, 0, decltype(opd)::LOADS * (B_INTO_LDS ? 2 : 1)>();
         else
           sched_kstep<IGLP, NM / 2, NR, 0, 0>();
         __builtin_amdgcn_sched_barrier(0);
