@@ -494,12 +494,14 @@ struct FastGemm {
   // In the forward the A waves fetch W straight into LDS as well (the LDS
   // fetch moves ~44 GB/s per CU from L2 against ~39 through registers): 4%
   // faster, no W staging registers (204 VGPRs); with the B waves fetching W
-  // instead it was 11% slower.  The input gradient's W is MN-major and stays
-  // on the register path (transposed there).  With both operands MN-major
+  // instead it was 11% slower.  The four-wave 128x128 forward tile fetches
+  // both operands into LDS from all four waves (4096 -> 512 at 16384 tokens,
+  // FP32 out: 82-98 -> 72-74 us).  The input gradient's W is MN-major and
+  // stays on the register path (transposed there).  With both operands MN-major
   // (the weight gradient) each role stages its own operand: the A waves have
   // no registers for both transposed operands (23 VGPRs spilled, 60% slower).
-  static constexpr bool A_INTO_LDS = !X3 && ROLE != ROLE_BOTH && A_KMAJ;
-  static constexpr bool DMA = A_INTO_LDS && ROLE == ROLE_A;               // this wave fetches A
+  static constexpr bool A_INTO_LDS = !X3 && A_KMAJ && (ROLE != ROLE_BOTH || B_KMAJ);
+  static constexpr bool DMA = A_INTO_LDS && ROLE != ROLE_B;               // this wave fetches A
   static constexpr bool DO_A = !A_INTO_LDS && ROLE != ROLE_B;             // A through registers
   static constexpr bool B_INTO_LDS = A_INTO_LDS && B_KMAJ;                // forward: W fetched by the A waves too
   static constexpr bool DO_B = B_INTO_LDS ? false : (A_INTO_LDS ? ROLE == ROLE_A : ROLE != ROLE_A);  // B through registers
