@@ -501,7 +501,7 @@ struct FastGemm {
   // (the weight gradient) each role stages its own operand: the A waves have
   // no registers for both transposed operands (23 VGPRs spilled, 60% slower).
   static constexpr bool A_INTO_LDS = !X3 && A_KMAJ && (ROLE != ROLE_BOTH || B_KMAJ);
-  static constexpr bool DMA = A_INTO_LDS && ROLE != ROLE_B;               // this wave fetches A
+  static constexpr bool DMA = A_INTO_LDS && ROLE != ROLE_B;               // this wave fetches A (and W, B_INTO_LDS)
   static constexpr bool DO_A = !A_INTO_LDS && ROLE != ROLE_B;             // A through registers
   static constexpr bool B_INTO_LDS = A_INTO_LDS && B_KMAJ;                // forward: W fetched by the A waves too
   static constexpr bool DO_B = B_INTO_LDS ? false : (A_INTO_LDS ? ROLE == ROLE_A : ROLE != ROLE_A);  // B through registers
