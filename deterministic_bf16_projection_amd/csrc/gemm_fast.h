@@ -472,7 +472,21 @@ struct FastGemm {
   static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
   static_assert(WM % 64 == 0 && WN % 64 == 0, "fragment swizzle parity follows the fragment index");
   static_assert(!X3 || ROLE == ROLE_BOTH, "BF16x3 runs on the four-wave tile");
-  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int FM0 = WM / 32, FN = WN / 32;
+  // Rows of the tile per role.  In the input gradient the staging waves
+  // (0-3) are the late ones even with the issue priority (timed inside the
+  // kernel: waves 4-7 waited 18% of the loop at the barrier, waves 0-3 7%),
+  // so there waves 0-3 compute 96 of the 256 rows and waves 4-7 160: 1.5-2.4%
+  // faster over four interleaved repeats, bitwise equal (64 / 192 rows was
+  // level).  Elsewhere each role computes WM rows.
+  static constexpr bool SPLIT_ROWS = ROLE != ROLE_BOTH && !X3 && A_KMAJ && !B_KMAJ;
+  static constexpr int FM = SPLIT_ROWS ? (ROLE == ROLE_A ? FM0 - 1 : FM0 + 1) : FM0;
+  // first row of this wave's part of the tile, and the swizzle parity of its
+  // first fragment (fragment rows 32 q + l carry fswz(l) ^ 4 (q & 1))
+  static __device__ __forceinline__ int row_start(int wm) {
+    return SPLIT_ROWS ? (ROLE == ROLE_A ? 0 : (FM0 - 1) * 32) : wm * WM;
+  }
+  static constexpr int PAR = (SPLIT_ROWS && ROLE == ROLE_B) ? ((FM0 - 1) & 1) : 0;
   // BF16x3: every operand has a hi and a lo plane (A hi, A lo, B hi, B lo)
   static constexpr int PLANES = X3 ? 2 : 1;
   static constexpr int PLANE_A = BM * BK, PLANE_B = BN * BK, STAGE = (PLANE_A + PLANE_B) * PLANES;
@@ -556,7 +570,7 @@ struct FastGemm {
     const int rr = lane >> 3, cc = lane & 7;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int m0 = row0 + wm * WM + i * 32;
+      const int m0 = row0 + row_start(wm) + i * 32;
       if constexpr (EOUT == OUT_BF16) {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
@@ -660,13 +674,13 @@ struct FastGemm {
 
     // fragment read offsets (elements) for this lane: row part and chunk part
     const int lr = lane & 31, lh = lane >> 5;
-    // fragment rows start at multiples of 32 (wave tiles at multiples of 64):
-    // fragment i sits at pattern fswz(lr) ^ 4 (i & 1), so it reads chunk
-    // (2 S + lh) at koff[S ^ 2 (i & 1)]
+    // fragment rows start at multiples of 32: fragment i sits at pattern
+    // fswz(lr) ^ 4 ((i + PAR) & 1), so it reads chunk (2 S + lh) at
+    // koff[S ^ 2 ((i + PAR) & 1)]
     const int sw = fswz(lr);
     int a_row[FM], b_row[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) a_row[i] = (wm * WM + i * 32 + lr) * 64;
+    for (int i = 0; i < FM; ++i) a_row[i] = (row_start(wm) + i * 32 + lr) * 64;
 #pragma unroll
     for (int j = 0; j < FN; ++j) b_row[j] = B_BASE + (wn * WN + j * 32 + lr) * 64;
     int koff[4];
@@ -677,9 +691,9 @@ struct FastGemm {
     bf16x8 fal[2][FM], fbl[2][FN];  // BF16x3 lo fragments
 #define DPG_READ_A(stage, S, BUF, i)                                                                         \
   do {                                                                                                     \
-    fa[BUF][i] = as_bf16x8(*(const u32x4*)((stage) + a_row[i] + koff[(S) ^ (2 * ((i) & 1))]));             \
+    fa[BUF][i] = as_bf16x8(*(const u32x4*)((stage) + a_row[i] + koff[(S) ^ (2 * (((i) + PAR) & 1))]));             \
     if constexpr (X3)                                                                                      \
-      fal[BUF][i] = as_bf16x8(*(const u32x4*)((stage) + PLANE_A + a_row[i] + koff[(S) ^ (2 * ((i) & 1))])); \
+      fal[BUF][i] = as_bf16x8(*(const u32x4*)((stage) + PLANE_A + a_row[i] + koff[(S) ^ (2 * (((i) + PAR) & 1))])); \
   } while (0)
 #define DPG_READ_B(stage, S, BUF, j)                                                                         \
   do {                                                                                                     \
@@ -757,7 +771,7 @@ struct FastGemm {
   _Pragma("unroll") for (int j = 0; j < FN; ++j) fb[BUF][j] =                                              \
       as_bf16x8(*(const u32x4*)((stage) + b_row[j] + koff[(S) ^ (2 * (j & 1))]))
 #define DPG_SB_READ_A(stage, S, i) \
-  fa1[i] = as_bf16x8(*(const u32x4*)((stage) + a_row[i] + koff[(S) ^ (2 * ((i) & 1))]))
+  fa1[i] = as_bf16x8(*(const u32x4*)((stage) + a_row[i] + koff[(S) ^ (2 * (((i) + PAR) & 1))]))
 #define DPG_SB_ROW(BUF, i) \
   _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(fb[BUF][j], fa1[i], acc[i][j])
     if constexpr (SB) {
