@@ -473,13 +473,15 @@ struct FastGemm {
   static_assert(WM % 64 == 0 && WN % 64 == 0, "fragment swizzle parity follows the fragment index");
   static_assert(!X3 || ROLE == ROLE_BOTH, "BF16x3 runs on the four-wave tile");
   static constexpr int FM0 = WM / 32, FN = WN / 32;
-  // Rows of the tile per role.  In the input gradient the staging waves
-  // (0-3) are the late ones even with the issue priority (timed inside the
-  // kernel: waves 4-7 waited 18% of the loop at the barrier, waves 0-3 7%),
-  // so there waves 0-3 compute 96 of the 256 rows and waves 4-7 160: 1.5-2.4%
-  // faster over four interleaved repeats, bitwise equal (64 / 192 rows was
-  // level).  Elsewhere each role computes WM rows.
-  static constexpr bool SPLIT_ROWS = ROLE != ROLE_BOTH && !X3 && A_KMAJ && !B_KMAJ;
+  // Rows of the tile per role.  Where waves 0-3 fetch A straight into LDS
+  // (forward, input gradient) they are the late ones even with the issue
+  // priority (timed inside the kernel, input gradient: waves 4-7 waited 18%
+  // of the loop at the barrier, waves 0-3 7%; forward 9% and 5%), so there
+  // waves 0-3 compute 96 of the 256 rows and waves 4-7 160: input gradient
+  // 1.5-2.4%, forward 1.2-1.8% faster over four interleaved repeats, bitwise
+  // equal (64 / 192 rows was level for the input gradient).  Elsewhere each
+  // role computes WM rows.
+  static constexpr bool SPLIT_ROWS = ROLE != ROLE_BOTH && !X3 && A_KMAJ;
   static constexpr int FM = SPLIT_ROWS ? (ROLE == ROLE_A ? FM0 - 1 : FM0 + 1) : FM0;
   // first row of this wave's part of the tile, and the swizzle parity of its
   // first fragment (fragment rows 32 q + l carry fswz(l) ^ 4 (q & 1))
