@@ -488,6 +488,57 @@ def test_twenty_reruns_bitwise():
         assert torch.equal(again.view(torch.int32), first.view(torch.int32))
 
 
+# One point of every workload, 20 reruns each, in each mode the workload
+# names (the pages qualify a point with repeated runs): every rerun must be
+# bitwise equal to the first.  Between reruns a 256 MB fill runs, so the
+# caches hold other data each time.
+RERUN_CASES = [
+    ("cfg1", "fwd", (64, 1024, 4096), "bf16", [(True, 0)]),
+    ("cfg1", "dgrad", (64, 1024, 4096), "bf16", [(True, 0)]),
+    ("cfg1", "wgrad", (64, 1024, 4096), "bf16", [(True, 0)]),
+    ("cfg2", "fwd", (256, 256, 4096), "router", [(True, 0), (False, 0)]),
+    ("cfg2", "dgrad", (1024, 256, 4096), "router", [(True, 0), (False, 0)]),
+    ("cfg2", "wgrad", (64, 256, 4096), "router", [(True, 0), (False, 0)]),
+    ("cfg3", "fwd", (16384, 12288, 4096), "bf16", [(True, 0)]),
+    ("cfg3", "dgrad", (16231, 12288, 4096), "f32", [(True, 0)]),
+    ("cfg3", "wgrad", (16384, 12288, 4096), "bf16", [(True, 0)]),
+    ("cfg4", "wgrad", (16173, 64, 4096), "bf16", [(True, 0), (False, 1), (False, 2)]),
+    ("cfg4", "wgrad", (65537, 48, 5120), "f32", [(True, 0), (False, 1), (False, 2)]),
+    ("cfg5", "fwd", (16384, 1024, 4096), "f32", [(True, 0)]),
+    ("cfg5", "dgrad", (16384, 512, 4096), "f32", [(True, 0)]),
+    ("cfg5", "wgrad", (16384, 1024, 4096), "f32", [(True, 0)]),
+]
+
+
+@pytest.mark.parametrize("cfg,pass_name,shape,out_name,modes", RERUN_CASES,
+                         ids=["%s-%s-%d" % (c[0], c[1], c[2][0]) for c in RERUN_CASES])
+def test_twenty_reruns_every_workload(cfg, pass_name, shape, out_name, modes):
+    T, N, K = shape
+    fill = torch.empty(1 << 26, dtype=torch.float32, device="cuda")
+    if out_name == "router":
+        x, w, dy = dpg_inputs.router(T, N, K, seed_group=3)
+        a, b = {"fwd": (x, w), "dgrad": (dy, w), "wgrad": (dy, x)}[pass_name]
+        da, db = dev_f32(a), dev_f32(b)
+        fn = {"fwd": dpg.dpg_router_forward, "dgrad": dpg.dpg_router_dgrad, "wgrad": dpg.dpg_router_wgrad}[pass_name]
+        call = lambda det, split: fn(da, db, deterministic=det, split_k=split)
+    else:
+        x, w, dy = dpg_inputs.dense(T, N, K, seed_group=3)
+        a, b = _operands(pass_name, x, w, dy)
+        da, db = dev_bf16(a), dev_bf16(b)
+        del x, w, dy, a, b
+        call = lambda det, split: _run(pass_name, da, db, OUT[out_name], det=det, split=split)
+    for det, split in modes:
+        first = call(det, split)
+        view = torch.int16 if first.dtype == torch.bfloat16 else torch.int32
+        for r in range(20):
+            fill.fill_(float(r))
+            again = call(det, split)
+            torch.cuda.synchronize()
+            assert torch.equal(again.view(view), first.view(view)), (cfg, pass_name, shape, det, split, r)
+            del again
+        del first
+
+
 def test_other_stream_and_graph_replay():
     T, N, K = 1025, 64, 4096
     x, w, dy = dpg_inputs.dense(T, N, K, seed_group=2)
