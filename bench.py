@@ -622,15 +622,42 @@ class ColdTimer:
     flush="read" flushes by reading the 1 GiB buffer instead (a sum): the
     caches then hold clean lines, whereas after the fill up to ~290 MB of dirty
     lines (L2 + Infinity Cache) are written back to HBM while the timed call
-    runs, which a short HBM-bound call pays for in full."""
+    runs, which a short HBM-bound call pays for in full.
 
-    def __init__(self, torch, groups=15, iters=20, warmup=5):
+    With spans=True the protocol runs again under torch's profiler
+    (span_groups groups of iters calls, no events), and `last_span` holds the
+    median of group medians of the call's kernel span: first kernel start to
+    last kernel end of the library's kernels between two flushes, from the
+    device timestamps (the pages time the span of an op's launches).  The
+    events also hold the dispatch of the call (2-5 us); the span does not.
+    None where the call runs no library kernel."""
+
+    def __init__(self, torch, groups=15, iters=20, warmup=5, spans=True, span_groups=5):
         self.torch = torch
         self.groups, self.iters, self.warmup = groups, iters, warmup
+        self.spans, self.span_groups = spans, span_groups
+        self.last_span = None
         self.junk = torch.empty(1 << 28, dtype=torch.float32, device="cuda:0")
         self.junk.zero_()
         n = groups * iters
         self.ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+
+    def _kernel_spans(self, prof):
+        """Span of each call: the library's kernels (names in namespace dpg)
+        that run between two flushes."""
+        cuda = self.torch.autograd.DeviceType.CUDA
+        ks = sorted((e.time_range.start, e.time_range.end, "dpg::" in e.name) for e in prof.events()
+                    if e.device_type == cuda)
+        spans, cur = [], None
+        for s, t, mine in ks:
+            if mine:
+                cur = [s, t] if cur is None else [cur[0], max(cur[1], t)]
+            elif cur is not None:
+                spans.append(cur[1] - cur[0])
+                cur = None
+        if cur is not None:
+            spans.append(cur[1] - cur[0])
+        return spans
 
     def _flush(self, flush):
         if flush == "zero":
@@ -656,6 +683,20 @@ class ColdTimer:
                 e1.record(stream)
             torch.cuda.synchronize()
             medians.append(float(np.median([e0.elapsed_time(e1) * 1e3 for e0, e1 in evs])))
+        self.last_span = None
+        if self.spans:
+            # a separate run under the profiler (its callbacks would shift the
+            # event times above), span_groups groups of iters calls
+            from torch.profiler import profile, ProfilerActivity
+            with profile(activities=[ProfilerActivity.CUDA]) as prof:
+                for _ in range(self.span_groups * self.iters):
+                    self._flush(flush)
+                    fn()
+                torch.cuda.synchronize()
+            spans = self._kernel_spans(prof)
+            if len(spans) == self.span_groups * self.iters:
+                sm = [float(np.median(spans[g * self.iters:(g + 1) * self.iters])) for g in range(self.span_groups)]
+                self.last_span = (float(np.median(sm)), min(sm), max(sm))
         return float(np.median(medians)), min(medians), max(medians)
 
     def close(self):
@@ -695,6 +736,8 @@ def cold_cache_passes(passes, cold):
         us, lo, hi = cold(fn)
         out[name] = {"us_median": round(us, 1), "group_median_range_us": [round(lo, 1), round(hi, 1)],
                      "tflops": round(flop / us / 1e6, 1), "frac_peak": round(flop / us / 1e6 / PEAK_BF16_TFLOPS, 4)}
+        if cold.last_span:
+            out[name]["us_span_median"] = round(cold.last_span[0], 1)
     return out
 
 
@@ -786,7 +829,9 @@ def skinny_sweep(dpg, dpg_inputs, torch, to_dev, cold):
                     call = (lambda det=det, split=split, ws=ws, out=out:
                             dpg.dpg_wgrad(dys, xs, out=out, deterministic=det, split_k=split, workspace=ws))
                     us, lo, hi = cold(call)
+                    span = cold.last_span
                     rus, _, _ = cold(call, flush="read")
+                    rspan = cold.last_span
                     nbytes = 2.0 * T_S * K + 2.0 * T_S * N + ob * N * K
                     plan = dpg.parse_plan(dpg.plan_describe(dpg.PASS_WGRAD, T_S, N, K, out_dtype, det, split))
                     row = {"shape": "%d->%d" % (K, N), "T": T_S, "out": oname,
@@ -796,6 +841,11 @@ def skinny_sweep(dpg, dpg_inputs, torch, to_dev, cold):
                            "us_cold_read_flush": round(rus, 2),
                            "frac_hbm_read_flush": round(nbytes / rus / 1e3 / PEAK_HBM_GBPS, 4),
                            "splits": int(plan["splits"]), "unit": plan["tile"], "grid": int(plan["grid"])}
+                    if span and rspan:
+                        row.update({"us_span_cold": round(span[0], 2),
+                                    "frac_hbm_span": round(nbytes / span[0] / 1e3 / PEAK_HBM_GBPS, 4),
+                                    "us_span_read_flush": round(rspan[0], 2),
+                                    "frac_hbm_span_read_flush": round(nbytes / rspan[0] / 1e3 / PEAK_HBM_GBPS, 4)})
                     if det and oname == "f32" and T_S in (16384, 65537):
                         reps = 50
                         for _ in range(5):
@@ -935,11 +985,13 @@ def secondary_configs(dpg, dpg_inputs, torch, to_dev, cold):
         for name, fn in ops:
             e1, g1 = timed([fn], reps=10)
             cus, _, _ = cold(fn)
+            cspan = cold.last_span
             p = dpg.parse_plan(dpg.plan_describe({"fwd": 0, "dgrad": 1, "wgrad": 2}[name], T, N, K, torch.float32))
             rec["ops"][name] = {"us_graph": g1, "tflops_graph": round(flop_op / g1 / 1e6, 1),
                                 "frac_peak_graph": round(flop_op / g1 / 1e6 / PEAK_BF16_TFLOPS, 4),
                                 "us_cold_median": round(cus, 1),
                                 "frac_peak_cold": round(flop_op / cus / 1e6 / PEAK_BF16_TFLOPS, 4),
+                                "us_span_cold": round(cspan[0], 1) if cspan else None,
                                 "plan": "%s %s splits=%s" % (p["kernel"], p["tile"], p["splits"])}
             cnt = read_step5_counters(N, name)
             if cnt:
@@ -957,6 +1009,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--skip-skinny", action="store_true")
+    ap.add_argument("--no-spans", action="store_true",
+                    help="cold-cache timings without torch's profiler (kernel spans), e.g. under rocprofv3")
     ap.add_argument("--skip-secondary", action="store_true", help="skip the small, router and step timings")
     ap.add_argument("--profile-run", action="store_true", help="one step + a 1 GiB calibration copy (for rocprofv3)")
     ap.add_argument("--clock-load", type=float, metavar="SECONDS",
@@ -1079,7 +1133,7 @@ def main():
     if busy:
         roofline["counters"] = busy
     progress("timed steps done")
-    cold = ColdTimer(torch)
+    cold = ColdTimer(torch, spans=not args.no_spans)
     passes_cold = cold_cache_passes(passes, cold)
     progress("cold-cache passes done")
     more = config3_more(dpg, torch, X, W, DY, Y, DX, DW, passes)
