@@ -421,3 +421,30 @@ def test_batched_validation_errors():
     assert fwd(*args(4100, 0, 4096)) == 3             # batch stride not 16-byte aligned
     assert fwd(*args(4096, 0, 4096, wl=5)) == 1       # bad layout
     assert fwd(FAKE, 64, 4096, FAKE, 64, 0, 0, FAKE, 64, 4096, BF16, -1, 64, 64, 64, 1, 0, None, 0, None) == 1
+
+
+def _edges(pass_, N, K, out, t_max):
+    from tests.plan_windows import plan_key
+    prev, edges = None, []
+    for T in range(1, t_max + 1):
+        k = plan_key(dpg.plan_describe(pass_, T, N, K, out, True, 0))
+        if prev is not None and k != prev:
+            edges.append(T)
+        prev = k
+    return edges
+
+
+def test_plan_windows_are_the_listed_ones():
+    """The deterministic plans change exactly at the T values the window-edge
+    GPU tests check (both sides of each)."""
+    import torch
+    from tests import plan_windows as pw
+    for (K, N), edges in pw.SKINNY_EDGES.items():
+        for out in (torch.bfloat16, torch.float32):
+            assert _edges(dpg.PASS_WGRAD, N, K, out, pw.SKINNY_T_MAX) == edges, (K, N, out)
+    for op, edges in pw.ROUTER_EDGES.items():
+        p = {"fwd": dpg.PASS_ROUTER_FORWARD, "dgrad": dpg.PASS_ROUTER_DGRAD, "wgrad": dpg.PASS_ROUTER_WGRAD}[op]
+        assert _edges(p, 256, 4096, torch.float32, pw.ROUTER_T_MAX) == edges, op
+    for op, edges in pw.SMALL_EDGES.items():
+        p = {"fwd": dpg.PASS_FORWARD, "dgrad": dpg.PASS_DGRAD, "wgrad": dpg.PASS_WGRAD}[op]
+        assert _edges(p, 1024, 4096, torch.bfloat16, pw.SMALL_T_MAX) == edges, op
