@@ -12,10 +12,10 @@ planner's windows are exactly these."""
 # skinny weight gradient dW[N, K] (K -> N), BF16 and FP32 output alike; the
 # plan stays the same from the last edge on (checked up to T = 70000)
 SKINNY_EDGES = {
-    (4096, 64): [1985, 3009, 4033, 5057, 6081, 7105, 8129],
-    (4096, 128): [1985, 3009, 4033, 5057, 6081, 7105, 8129],
-    (5120, 48): [1985, 3009, 4033, 5057, 6081],
-    (5120, 64): [1985, 3009, 4033, 5057, 6081],
+    (4096, 64): [1473, 1985, 2497, 3009, 3521, 4033],
+    (4096, 128): [1473, 1985, 2497, 3009, 3521, 4033],
+    (5120, 48): [1473, 1985, 2497, 3009],
+    (5120, 64): [1473, 1985, 2497, 3009],
 }
 SKINNY_T_MAX = 70000
 

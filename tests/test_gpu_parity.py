@@ -385,10 +385,10 @@ SKINNY_EXACT = [
     (16384, 48, 5120),   # one row block, ragged N inside the block
     (1025, 104, 1024),   # two row blocks, N ragged; 17 token blocks, last holds 1
     (16384, 128, 4096),  # two row blocks, 128-column units
-    (65537, 104, 3968),  # two row blocks, N ragged, 31 units of 128 columns, 16 splits
-    (16400, 40, 1000),   # one row block, N ragged, last 128-column unit partial, 16 splits of
-                         # 17 or 2 token blocks (one 16-token step per wave), last block 16 tokens
-    (16400, 104, 1000),  # the same with two row blocks, N ragged, 2 or 17 blocks a split
+    (65537, 104, 3968),  # two row blocks, N ragged, 31 units of 128 columns, 8 splits
+    (16400, 40, 1000),   # one row block, N ragged, last 128-column unit partial, 32 splits of
+                         # 9 or 8 token blocks, last block 16 tokens (29 16-token steps over 8 waves)
+    (16400, 104, 1000),  # the same with two row blocks, N ragged, 9 or 8 blocks a split
 ]
 
 

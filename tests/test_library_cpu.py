@@ -92,9 +92,13 @@ def test_skinny_unit_shapes():
     assert tile(65537, 128, 4096, 0, 2) == "128x64x64"
     assert tile(32768, 104, 4096, 1, 0) == "128x128x64"
     p = plan(2, 16400, 40, 1000, out=F32, det=1, split=0)
-    assert p["tile"] == "64x128x64" and p["splits"] == "16" and p["kt_per_split"] == "17", p
+    assert p["tile"] == "64x128x64" and p["splits"] == "32" and p["kt_per_split"] == "9", p
     p = plan(2, 16400, 104, 1000, out=F32, det=1, split=0)
-    assert p["tile"] == "128x128x64" and p["splits"] == "16" and p["kt_per_split"] == "17", p
+    assert p["tile"] == "128x128x64" and p["splits"] == "32" and p["kt_per_split"] == "9", p
+    # at least 8 token blocks a split from 24 blocks on, 16 below
+    assert plan(2, 1472, 64, 4096, out=F32)["splits"] == "1"
+    assert plan(2, 1473, 64, 4096, out=F32)["splits"] == "3"
+    assert plan(2, 4031, 64, 4096, out=F32)["splits"] == "7"
     seen = set()
     for T, N, K in [(4031, 128, 4096), (16384, 48, 5120), (1025, 104, 1024), (16384, 128, 4096), (65537, 104, 3968),
                     (16400, 40, 1000), (16400, 104, 1000)]:
