@@ -13,14 +13,19 @@ namespace dpg {
 // kernel, while the 128x128 tile gains from its second workgroup: FP32-output
 // projections at 16384 tokens ran at 0.40-0.45 of the CU rate with two per CU,
 // against 0.26-0.41 with one depending on layout).  BF16x3 plans use the
-// pipelined 128x128 tile or the generic 64x64 one.
+// pipelined 128x128 tile or the generic 64x64 one.  Two generic BF16x3
+// workgroups on a CU with short units (up to 8 K tiles) run faster than the
+// one-workgroup rate says: router forward (hidden 4096) at 768 and 1024 tokens,
+// 8 splits on 64x64 tiles, 19.8 and 22.2 us measured against 25 us modelled;
+// with longer units the one-workgroup rate fits (1200-2048 tokens, where the
+// pipelined 128x128 tile with 8-12 splits is faster).
 const TileShape kTiles[kNumTiles] = {
-    // bm, bn, bk, threads, occupancy, eff, eff_one, x3_eff, x3_occupancy, x3_ok, fast_ok, ffma
-    {256, 256, 64, 256, 1, 0.55, 0.0, 0.0, 0, false, true, false},
-    {128, 128, 64, 256, 2, 0.43, 0.36, 0.28, 1, true, true, false},
-    {64, 64, 64, 256, 4, 0.20, 0.0, 0.19, 2, true, false, false},
+    // bm, bn, bk, threads, occupancy, eff, eff_one, x3_eff, x3_eff_two, x3_occupancy, x3_ok, fast_ok, ffma
+    {256, 256, 64, 256, 1, 0.55, 0.0, 0.0, 0.0, 0, false, true, false},
+    {128, 128, 64, 256, 2, 0.43, 0.36, 0.28, 0.0, 1, true, true, false},
+    {64, 64, 64, 256, 4, 0.20, 0.0, 0.19, 0.26, 2, true, false, false},
     // FP32 FMA (router): eff is the fraction of the CU's FP32 vector rate
-    {64, 64, 64, 256, 4, 0.35, 0.0, 0.0, 0, false, false, true},
+    {64, 64, 64, 256, 4, 0.35, 0.0, 0.0, 0.0, 0, false, false, true},
 };
 
 namespace {
@@ -80,7 +85,9 @@ double estimate_us(const TileShape& ts, bool fast, int64_t batch, int64_t M, int
   const int64_t rounds = cdiv(units, (int64_t)cus * occ_used);
   // a lone four-wave workgroup leaves the CU's MFMA pipes idler than two do
   const double eff = (occ_used == 1 && ts.eff_one > 0) ? ts.eff_one : ts.eff;
-  const double cu_rate = ts.ffma ? kCuFp32 * ts.eff : kCuFlops * (x3 ? ts.x3_eff : eff);
+  // two short BF16x3 units (up to 8 K tiles) on a CU overlap each other's fill and drain
+  const double x3_eff = (occ_used == 2 && ts.x3_eff_two > 0 && kt_per <= 8) ? ts.x3_eff_two : ts.x3_eff;
+  const double cu_rate = ts.ffma ? kCuFp32 * ts.eff : kCuFlops * (x3 ? x3_eff : eff);
   const double epi_us = (double)occ_used * ts.bm * ts.bn * (s > 1 ? 4 : out_bytes) / kCuStore * 1e6;
   const double mfma_round_us = (double)occ_used * flop_unit / cu_rate * 1e6;
   double t_gemm = fast ? rounds * mfma_round_us + kUnitUs + epi_us : rounds * (mfma_round_us + kUnitUs + epi_us);

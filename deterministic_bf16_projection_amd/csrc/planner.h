@@ -18,6 +18,7 @@ struct TileShape {
   double eff;      // sustained fraction of the CU's MFMA rate, BF16 operands (model)
   double eff_one;  // the same when only one of its workgroups runs on a CU (0: as eff)
   double x3_eff;   // the same for BF16x3 (FP32 operands), counted in executed FLOP
+  double x3_eff_two;  // BF16x3 with two workgroups on each CU (0: as x3_eff)
   int x3_occupancy;  // workgroups per CU with BF16x3 (hi and lo planes)
   bool x3_ok;      // BF16x3 plans use this tile
   bool fast_ok;    // a software-pipelined variant exists for this tile
