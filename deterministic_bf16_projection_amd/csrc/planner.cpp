@@ -14,10 +14,13 @@ namespace dpg {
 // projections at 16384 tokens ran at 0.40-0.45 of the CU rate with two per CU,
 // against 0.26-0.41 with one depending on layout).  BF16x3 plans use the
 // pipelined 128x128 tile or the generic 64x64 one.  Two generic BF16x3
-// workgroups on a CU with short units (up to 8 K tiles) run faster than the
-// one-workgroup rate says: router forward (hidden 4096) at 768 and 1024 tokens,
-// 8 splits on 64x64 tiles, 19.8 and 22.2 us measured against 25 us modelled;
-// with longer units the one-workgroup rate fits (1200-2048 tokens, where the
+// workgroups on a CU run faster than the one-workgroup rate says in the
+// weight-gradient layout and, in the K-major layouts, with short units (up to
+// 10 K tiles): router forward (hidden 4096) at 768 and 1024 tokens, 8 splits
+// on 64x64 tiles, 19.9 and 21.9 us measured against 25 us modelled; router
+// weight gradient at 1760-2048 tokens, 2 splits on 64x64 tiles 31.6-34.2 us
+// against 37.3-40.2 us for the 128x128 tile the one-workgroup rate chose.
+// With longer forward units that rate fits (1200-2048 tokens, where the
 // pipelined 128x128 tile with 8-12 splits is faster).
 const TileShape kTiles[kNumTiles] = {
     // bm, bn, bk, threads, occupancy, eff, eff_one, x3_eff, x3_eff_two, x3_occupancy, x3_ok, fast_ok, ffma
@@ -73,7 +76,8 @@ void gemm_view(int pass, int wlayout, int64_t T, int64_t N, int64_t K, int64_t* 
 // back by the reduce kernel, whose dependent loads cost latency when the
 // output is small.
 double estimate_us(const TileShape& ts, bool fast, int64_t batch, int64_t M, int64_t N, int64_t K, int x3,
-                   int out_bytes, int in_bytes, int splits_req, int cus, int* splits_out, int* kt_per_out) {
+                   int layout, int out_bytes, int in_bytes, int splits_req, int cus, int* splits_out,
+                   int* kt_per_out) {
   const int64_t tiles = cdiv(M, ts.bm) * cdiv(N, ts.bn) * batch;
   const int64_t kt_total = cdiv(K, ts.bk);
   // balanced partition: min(request, K tiles) splits, the largest kt_per tiles
@@ -85,8 +89,10 @@ double estimate_us(const TileShape& ts, bool fast, int64_t batch, int64_t M, int
   const int64_t rounds = cdiv(units, (int64_t)cus * occ_used);
   // a lone four-wave workgroup leaves the CU's MFMA pipes idler than two do
   const double eff = (occ_used == 1 && ts.eff_one > 0) ? ts.eff_one : ts.eff;
-  // two short BF16x3 units (up to 8 K tiles) on a CU overlap each other's fill and drain
-  const double x3_eff = (occ_used == 2 && ts.x3_eff_two > 0 && kt_per <= 8) ? ts.x3_eff_two : ts.x3_eff;
+  // two BF16x3 workgroups on a CU: weight-gradient layout, or short units (up
+  // to 10 K tiles) of the K-major layouts
+  const bool two = occ_used == 2 && ts.x3_eff_two > 0 && (layout == LAYOUT_WGRAD || kt_per <= 10);
+  const double x3_eff = two ? ts.x3_eff_two : ts.x3_eff;
   const double cu_rate = ts.ffma ? kCuFp32 * ts.eff : kCuFlops * (x3 ? x3_eff : eff);
   const double epi_us = (double)occ_used * ts.bm * ts.bn * (s > 1 ? 4 : out_bytes) / kCuStore * 1e6;
   const double mfma_round_us = (double)occ_used * flop_unit / cu_rate * 1e6;
@@ -219,8 +225,8 @@ bool make_plan(const PlanKey& key, Plan* p) {
     }
     for (int c = 0; c < n_choices; ++c) {
       int s, ktp;
-      const double t = estimate_us(ts, fast, p->batch, p->M, p->N, p->K, ts.ffma ? 0 : p->x3, out_bytes, in_bytes,
-                                   choices[c], key.cus, &s, &ktp);
+      const double t = estimate_us(ts, fast, p->batch, p->M, p->N, p->K, ts.ffma ? 0 : p->x3, p->layout, out_bytes,
+                                   in_bytes, choices[c], key.cus, &s, &ktp);
       if (best_tile < 0 || t < best * 0.97) {  // prefer the earlier (larger tile, fewer splits) unless 3% faster
         best = t;
         best_tile = ti;

@@ -23,7 +23,7 @@ SKINNY_T_MAX = 70000
 ROUTER_EDGES = {
     "fwd": [129, 257, 321, 513, 641, 1025, 1281, 1345],
     "dgrad": [513],
-    "wgrad": [1729, 1793, 1921],
+    "wgrad": [1729, 1793, 1857],
 }
 ROUTER_T_MAX = 2048
 
