@@ -28,7 +28,12 @@ const TileShape kTiles[kNumTiles] = {
     {128, 128, 64, 256, 2, 0.43, 0.36, 0.28, 0.0, 1, true, true, false},
     {64, 64, 64, 256, 4, 0.20, 0.0, 0.19, 0.26, 2, true, false, false},
     // FP32 FMA (router): eff is the fraction of the CU's FP32 vector rate
-    {64, 64, 64, 256, 4, 0.35, 0.0, 0.0, 0.0, 0, false, false, true},
+    // with two or more workgroups on a CU, eff_one with one (a workgroup has
+    // one wave per SIMD, too few to cover its LDS and FMA latencies): router
+    // at 1024 tokens, forward 42.5 us with 8 splits (two per CU) against 62.8
+    // us with 4 (one per CU), weight gradient 40.9 us with 2 splits against
+    // 58.2 us with 1
+    {64, 64, 64, 256, 4, 0.42, 0.25, 0.0, 0.0, 0, false, false, true},
 };
 
 namespace {
@@ -93,7 +98,7 @@ double estimate_us(const TileShape& ts, bool fast, int64_t batch, int64_t M, int
   // to 10 K tiles) of the K-major layouts
   const bool two = occ_used == 2 && ts.x3_eff_two > 0 && (layout == LAYOUT_WGRAD || kt_per <= 10);
   const double x3_eff = two ? ts.x3_eff_two : ts.x3_eff;
-  const double cu_rate = ts.ffma ? kCuFp32 * ts.eff : kCuFlops * (x3 ? x3_eff : eff);
+  const double cu_rate = ts.ffma ? kCuFp32 * eff : kCuFlops * (x3 ? x3_eff : eff);
   const double epi_us = (double)occ_used * ts.bm * ts.bn * (s > 1 ? 4 : out_bytes) / kCuStore * 1e6;
   const double mfma_round_us = (double)occ_used * flop_unit / cu_rate * 1e6;
   double t_gemm = fast ? rounds * mfma_round_us + kUnitUs + epi_us : rounds * (mfma_round_us + kUnitUs + epi_us);
