@@ -187,8 +187,9 @@ bool make_plan(const PlanKey& key, Plan* p) {
     } else {
       s = (key.cus + units / 2) / units;
       // at least 8 token blocks a split (16 below 24 blocks, where one split
-      // was as fast): from a cold cache 2-4 more splits than 16 blocks a split
-      // allowed measured 5-18% faster at 3000-6000 tokens
+      // was as fast): from a cold cache the 2-4 more splits this allows than
+      // 16 blocks a split measured 0-12% faster at 1600-7105 tokens (kernel
+      // spans after a read flush; within -11..+6% after a zero fill)
       s = std::min<int64_t>(s, std::max<int64_t>(1, p->kt_total >= 24 ? p->kt_total / 8 : p->kt_total / 16));
     }
     // balanced partition of the 64-token blocks (split_begin in the kernels)
