@@ -45,6 +45,7 @@ constexpr double kLaunchUs = 3.0;          // per kernel launch
 constexpr double kUnitUs = 1.0;            // fixed latency of a unit (first loads, last MFMAs)
 constexpr double kCuStore = 25e9;          // bytes/s of epilogue stores per CU
 constexpr double kReduceLatUs = 0.5;       // split reduction: per group of 8 dependent plane loads
+constexpr double kWgFetch = 40e9;          // operand bytes/s one generic-kernel workgroup fetches
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -100,7 +101,15 @@ double estimate_us(const TileShape& ts, bool fast, int64_t batch, int64_t M, int
   const double x3_eff = two ? ts.x3_eff_two : ts.x3_eff;
   const double cu_rate = ts.ffma ? kCuFp32 * eff : kCuFlops * (x3 ? x3_eff : eff);
   const double epi_us = (double)occ_used * ts.bm * ts.bn * (s > 1 ? 4 : out_bytes) / kCuStore * 1e6;
-  const double mfma_round_us = (double)occ_used * flop_unit / cu_rate * 1e6;
+  double mfma_round_us = (double)occ_used * flop_unit / cu_rate * 1e6;
+  // the generic kernel stages through registers without a deep pipeline: a
+  // workgroup's operand fetch, (bm + bn) x bk elements a K tile, bounds a long
+  // unit (32 K tiles or more; 4096 -> 1024 forward at 1024 tokens, one split
+  // on 64x64 tiles: 40.4 us measured against 23.9 us from the MFMA rate
+  // alone; the 128x128 tile with 4 splits ran 22.8 us).  Shorter units ran
+  // at the MFMA rate.
+  if (!fast && !ts.ffma && kt_per >= 32)
+    mfma_round_us = std::max(mfma_round_us, (double)(ts.bm + ts.bn) * kt_per * ts.bk * in_bytes / kWgFetch * 1e6);
   double t_gemm = fast ? rounds * mfma_round_us + kUnitUs + epi_us : rounds * (mfma_round_us + kUnitUs + epi_us);
   const double bytes = ((double)(M * K + N * K) * in_bytes + (double)M * N * out_bytes) * batch;
   double t = std::max(t_gemm, bytes / kHbm * 1e6) + kLaunchUs;
