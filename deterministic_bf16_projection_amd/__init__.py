@@ -121,8 +121,17 @@ def _ld(t, name):
     return t.stride(0)
 
 
-def _stream(stream):
+# Raw handle of a device's current stream (the accessor torch's own compiler
+# uses): about 0.3 us a call against about 3 us for a torch.cuda.Stream object.
+_raw_current_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream(stream, device=None):
+    """HIP stream handle of a call: `stream` as given, else the current stream
+    of `device` (the device the call runs on, which is current there)."""
     if stream is None:
+        if _raw_current_stream is not None and device is not None and device.index is not None:
+            return _raw_current_stream(device.index)
         return torch.cuda.current_stream().cuda_stream
     if isinstance(stream, torch.cuda.Stream):
         return stream.cuda_stream
@@ -233,7 +242,8 @@ def _call(name, pass_, a, b, out, out_code, T, N, K, deterministic, split_k, wor
         args = [a.data_ptr(), _ld(a, "a"), b.data_ptr(), _ld(b, "b"), out.data_ptr(), _ld(out, "out")]
         if pass_ < 3:
             args.append(out_code)
-        args += [T, N, K, det, split_k, ws.data_ptr() if ws is not None else None, ws_bytes, _stream(stream)]
+        args += [T, N, K, det, split_k, ws.data_ptr() if ws is not None else None, ws_bytes,
+                 _stream(stream, out.device)]
         st = fn(*args)
     if st:
         raise DpgError(st, name)
@@ -341,7 +351,7 @@ def dpg_wgrad_noalloc(dy, x, out, deterministic=True, split_k=0, stream=None):
     with _on_device(out.device):
         st = _lib.dpg_wgrad_noalloc(dy.data_ptr(), _ld(dy, "dy"), x.data_ptr(), _ld(x, "x"), out.data_ptr(),
                                     _ld(out, "out"), _code(out.dtype), T, N, K, int(bool(deterministic)), split_k,
-                                    _stream(stream))
+                                    _stream(stream, out.device))
     if st:
         raise DpgError(st, "dpg_wgrad_noalloc")
     return out
@@ -494,7 +504,7 @@ def dpg_forward_batched(x, w, out=None, out_dtype=torch.bfloat16, weight_layout=
                                   x.device)
         st = _lib.dpg_forward_batched(x3.data_ptr(), ldx, sx, w3.data_ptr(), ldw, sw, wl, o3.data_ptr(), ldo, so,
                                       _code(out.dtype), batch, T, N, K, det, split_k,
-                                      ws.data_ptr() if ws is not None else None, wsb, _stream(stream))
+                                      ws.data_ptr() if ws is not None else None, wsb, _stream(stream, x.device))
     if st:
         raise DpgError(st, "dpg_forward_batched")
     return out
@@ -526,7 +536,7 @@ def dpg_dgrad_batched(dy, w, out=None, out_dtype=torch.bfloat16, weight_layout="
                                   dy.device)
         st = _lib.dpg_dgrad_batched(d3.data_ptr(), ldd, sd, w3.data_ptr(), ldw, sw, wl, o3.data_ptr(), ldo, so,
                                     _code(out.dtype), batch, T, N, K, det, split_k,
-                                    ws.data_ptr() if ws is not None else None, wsb, _stream(stream))
+                                    ws.data_ptr() if ws is not None else None, wsb, _stream(stream, dy.device))
     if st:
         raise DpgError(st, "dpg_dgrad_batched")
     return out
@@ -559,7 +569,7 @@ def dpg_wgrad_batched(dy, x, out=None, out_dtype=torch.bfloat16, weight_layout="
                                   dy.device)
         st = _lib.dpg_wgrad_batched(d3.data_ptr(), ldd, sd, x3.data_ptr(), ldx, sx, o3.data_ptr(), ldo, so, wl,
                                     _code(out.dtype), batch, T, N, K, det, split_k,
-                                    ws.data_ptr() if ws is not None else None, wsb, _stream(stream))
+                                    ws.data_ptr() if ws is not None else None, wsb, _stream(stream, dy.device))
     if st:
         raise DpgError(st, "dpg_wgrad_batched")
     return out
