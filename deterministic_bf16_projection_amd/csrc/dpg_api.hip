@@ -682,7 +682,7 @@ const char* dpg_status_string(dpg_status status) {
   switch (status) {
     case DPG_OK: return "ok";
     case DPG_ERR_INVALID_ARG: return "invalid argument";
-    case DPG_ERR_UNSUPPORTED: return "unsupported split_k";
+    case DPG_ERR_UNSUPPORTED: return "unsupported: split_k outside 0..64, or a launch beyond the grid limit";
     case DPG_ERR_ALIGNMENT: return "pointer, leading dimension or column count not 16-byte compatible";
     case DPG_ERR_WORKSPACE: return "workspace missing or too small";
     case DPG_ERR_HIP: return "HIP launch failed";

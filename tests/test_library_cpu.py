@@ -452,3 +452,27 @@ def test_plan_windows_are_the_listed_ones():
     for op, edges in pw.SMALL_EDGES.items():
         p = {"fwd": dpg.PASS_FORWARD, "dgrad": dpg.PASS_DGRAD, "wgrad": dpg.PASS_WGRAD}[op]
         assert _edges(p, 1024, 4096, torch.bfloat16, pw.SMALL_T_MAX) == edges, op
+
+
+def test_describe_buffer_edges_and_stats_pointers():
+    """dpg_plan_describe truncates to buflen - 1 characters (NUL-terminated),
+    rejects a NULL or empty buffer; dpg_plan_cache_stats accepts NULL
+    pointers; every status has a text."""
+    full = ctypes.create_string_buffer(1024)
+    assert L.dpg_plan_describe(0, 64, 1024, 4096, BF16, 1, 0, full, 1024) == 0
+    text = full.value
+    assert text.startswith(b"pass=forward") and len(text) < 1023
+    for n in (1, 2, 17):
+        buf = ctypes.create_string_buffer(b"\xff" * 32, 32)
+        assert L.dpg_plan_describe(0, 64, 1024, 4096, BF16, 1, 0, buf, n) == 0
+        assert buf.raw[:n] == text[:n - 1] + b"\x00"
+        assert buf.raw[n:32] == b"\xff" * (32 - n)  # nothing past buflen
+    assert L.dpg_plan_describe(0, 64, 1024, 4096, BF16, 1, 0, None, 64) == 1
+    assert L.dpg_plan_describe(0, 64, 1024, 4096, BF16, 1, 0, full, 0) == 1
+    L.dpg_plan_cache_stats(None, None)
+    e = ctypes.c_int64(-1)
+    L.dpg_plan_cache_stats(ctypes.byref(e), None)
+    assert e.value >= 0
+    for st in range(0, 6):
+        assert L.dpg_status_string(st) and L.dpg_status_string(st) != b"unknown status"
+    assert L.dpg_status_string(99) == b"unknown status"
